@@ -1,0 +1,234 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a paged KV cache on AMD MI355X
+ * (gfx950), plus the host-side block pool and sequence bookkeeping.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [KV-prep]  "LLM Inference: KV Cache, Batching & Scheduling" (cariara.com)
+ *   [KV-news]  "LLM Inference Engineering: Overcoming the KV-Cache Bottleneck
+ *              and Maximizing Production Throughput" (wpnews.pro summary)
+ *   [KV-blog]  the adilsher.pro blog post of the same title
+ *
+ * Conventions for every call below:
+ *   - Device pointers are caller-owned, contiguous and 16-byte aligned; the
+ *     library never allocates, frees or retains device memory.
+ *   - Kernel calls enqueue on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return without synchronising.  A fault in a kernel shows up
+ *     at the caller's next synchronisation.
+ *   - Only host scalars and pointers are validated.  Contents of device
+ *     arrays (block ids, slots, lengths) are preconditions; kernels never
+ *     read or write outside the buffers the sizes describe: a block id
+ *     outside [0, num_blocks) contributes nothing, a slot outside the cache
+ *     is not written, and a context length is clamped to
+ *     block_table_stride * block_size.
+ *   - Return value: PKV_OK (0) or a negative PKV_E* code; pkv_last_error()
+ *     then holds a message for the calling thread.
+ *   - Element types: q, k, v and the caches share one dtype (PKV_F32 or
+ *     PKV_BF16); index arrays are int32.
+ *
+ * Cache layout (the pages fix none; this library's reading): each of
+ * k_cache and v_cache is [num_blocks][num_kv_heads][block_size][head_dim]
+ * elements, so one KV head's share of a block is one contiguous tile.  A slot
+ * s names block s / block_size, offset s % block_size.  Query head h reads KV
+ * head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define PKV_OK 0
+#define PKV_EINVAL (-1)       /* null pointer, bad size, misaligned pointer, short workspace */
+#define PKV_EUNSUPPORTED (-2) /* dtype / head_dim / block_size / group combination not built */
+#define PKV_ENOBLOCKS (-3)    /* block pool exhausted; the pool is left unchanged */
+#define PKV_ESTATE (-4)       /* bookkeeping misuse: unknown id, double release, write into a shared block */
+#define PKV_EHIP (-5)         /* HIP launch or runtime error */
+
+/* Element types. */
+#define PKV_F32 0
+#define PKV_BF16 1
+
+/* Shape of one layer's cache.  block_size: 16 or 32 ([KV-news] section 2,
+ * [KV-prep] "PagedAttention and vLLM").  head_dim: 64 or 128. */
+typedef struct pkv_cache_desc {
+    int32_t num_blocks;   /* physical blocks in each of k_cache, v_cache */
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t head_dim;
+    int32_t dtype;        /* PKV_F32 or PKV_BF16 */
+} pkv_cache_desc;
+
+/* Static text for a return code. */
+const char *pkv_strerror(int code);
+/* Detail message of the calling thread's last failed call ("" if none). */
+const char *pkv_last_error(void);
+/* ABI version of this header (bumped on incompatible change). */
+int pkv_abi_version(void);
+#define PKV_ABI_VERSION 1
+
+/* ------------------------------------------------------------------------
+ * KV append ([KV-prep] "The KV cache": the new token's K and V are appended
+ * each step).
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   slot_mapping  [num_tokens] int32; row t goes to slot slot_mapping[t];
+ *                 a negative slot skips the row.  Slots must be distinct.
+ *   k_cache, v_cache  the caches described by `c`
+ * Copies bits; no conversion.  num_tokens == 0 is a no-op.
+ */
+int pkv_append(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+               void *k_cache, void *v_cache, const pkv_cache_desc *c, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention ([KV-prep] "The KV cache": the query attends the
+ * keys and values of every prior position; [KV-news] section 2 and
+ * [KV-prep] "PagedAttention and vLLM": those positions live in fixed-size
+ * blocks that a per-sequence table maps from logical to physical).
+ *
+ * For sequence b and query head h (KV head g = h / G, G = num_q_heads /
+ * num_kv_heads), with L = context_lens[b] and key/value j read from block
+ * block_tables[b * block_table_stride + j / block_size], offset
+ * j % block_size:
+ *     out[b][h][:] = sum_j softmax_j(scale * q[b][h] . K_j) * V_j[:]
+ * over j in [0, L); L == 0 gives zeros.  Accumulation is fp32.
+ *
+ *   q             [num_seqs][num_q_heads][head_dim], cache dtype
+ *   block_tables  [num_seqs][block_table_stride] int32; entries past
+ *                 ceil(L / block_size) are not read
+ *   context_lens  [num_seqs] int32
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid;
+ *                 a sequence longer than it is a precondition violation)
+ *   out           [num_seqs][num_q_heads][head_dim]; out_dtype PKV_F32 or
+ *                 PKV_BF16 (round to nearest even)
+ *   partition_tokens  context tokens per split partition; 0 = library choice
+ *                 (pkv_decode_partition_tokens); otherwise a positive
+ *                 multiple of 4 * block_size
+ *   workspace     device scratch of at least pkv_decode_workspace_bytes(...)
+ *                 bytes for the split partials (fp32); may be NULL when that
+ *                 size is 0.  Its contents need no initialisation.
+ * Supported: dtype F32/BF16, head_dim 64/128, block_size 16/32,
+ * G in {1, 2, 4, 8}.
+ */
+int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t max_context_len, const pkv_cache_desc *c);
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                  int32_t partition_tokens, const pkv_cache_desc *c);
+int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, int32_t block_table_stride,
+               const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+               int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+               int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+               const pkv_cache_desc *c, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Causal chunked prefill ([KV-prep] "Chunked prefill": a prompt is split into
+ * fixed-size chunks, e.g. 512 tokens, interleaved with decode; the split does
+ * not change the result).
+ *
+ * Sequence b contributes C_b = query_start_loc[b+1] - query_start_loc[b]
+ * query rows; its chunk's K/V is already appended, so context_lens[b] (L_b)
+ * counts it.  Chunk row i (0 <= i < C_b) attends keys [0, L_b - C_b + i],
+ * diagonal included.  QK^T and PV run on bf16 MFMA with fp32 accumulation.
+ *
+ *   q                [query_start_loc[num_seqs]][num_q_heads][head_dim] bf16
+ *   query_start_loc  [num_seqs + 1] int32, non-decreasing, starts at 0
+ *   max_query_len    host-side upper bound of C_b
+ *   out              like q, out_dtype PKV_F32 or PKV_BF16
+ *   workspace        may be NULL when pkv_prefill_workspace_bytes(...) is 0
+ * Supported: dtype BF16 only (PKV_EUNSUPPORTED for F32), head_dim 64/128,
+ * block_size 16/32, G in {1, 2, 4, 8}.
+ */
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_query_len,
+                                   const pkv_cache_desc *c);
+int pkv_prefill_chunk(const void *q, const int32_t *query_start_loc, int32_t num_seqs,
+                      int32_t max_query_len, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, int32_t block_table_stride,
+                      const int32_t *context_lens, int32_t max_context_len,
+                      int32_t num_q_heads, float scale, void *out, int32_t out_dtype,
+                      void *workspace, size_t workspace_bytes, const pkv_cache_desc *c,
+                      void *stream);
+
+/* ------------------------------------------------------------------------
+ * Host block pool ([KV-prep] "PagedAttention and vLLM": pages are allocated
+ * on demand and a finished request's pages return to the pool at once;
+ * [KV-news] section 2 and [KV-blog] "The Elegant Fix": identical prefixes
+ * share pages).  Single-threaded; the caller owns the handle.
+ */
+typedef struct pkv_pool pkv_pool;
+
+/* seed 0: free list in ascending id order; otherwise a permutation drawn
+ * from the seed.  Returns NULL on bad arguments or allocation failure. */
+pkv_pool *pkv_pool_create(int32_t num_blocks, uint64_t seed);
+void pkv_pool_destroy(pkv_pool *pool);
+/* Pop n blocks from the front of the free list (refcount 1 each) into ids.
+ * All-or-nothing: PKV_ENOBLOCKS leaves the pool unchanged. */
+int pkv_pool_alloc(pkv_pool *pool, int32_t n, int32_t *ids);
+/* Add one reference to each of n allocated blocks (PKV_ESTATE if any is
+ * free or unknown; then nothing changes). */
+int pkv_pool_share(pkv_pool *pool, int32_t n, const int32_t *ids);
+/* Drop one reference from each of n blocks; a block reaching 0 returns to the
+ * back of the free list.  PKV_ESTATE if any id is free or unknown, or appears
+ * more often than its refcount; then nothing changes. */
+int pkv_pool_release(pkv_pool *pool, int32_t n, const int32_t *ids);
+int32_t pkv_pool_num_free(const pkv_pool *pool);
+int32_t pkv_pool_num_blocks(const pkv_pool *pool);
+/* Refcount of a block (0 = free), or -1 for an id outside the pool. */
+int32_t pkv_pool_refcount(const pkv_pool *pool, int32_t id);
+
+/* ------------------------------------------------------------------------
+ * Sequence bookkeeping over a pool (continuous batching, [KV-prep]
+ * "Continuous batching (Orca)": sequences join and leave at every step).
+ * A sequence is a caller-chosen int64 id with a length and a list of block
+ * ids.  The pool must outlive the set.
+ */
+typedef struct pkv_seqs pkv_seqs;
+
+typedef struct pkv_seqs_stats {
+    int32_t num_seqs;
+    int64_t blocks_referenced;   /* sum over sequences of their block counts */
+    int32_t blocks_in_use;       /* pool blocks with refcount > 0 */
+    int64_t tokens;              /* sum of lengths */
+    int64_t slots_unused;        /* reserved but unused slots in last blocks
+                                    ([KV-prep] "internal fragmentation") */
+} pkv_seqs_stats;
+
+pkv_seqs *pkv_seqs_create(pkv_pool *pool, int32_t block_size);
+void pkv_seqs_destroy(pkv_seqs *seqs);
+/* New empty sequence; PKV_ESTATE if the id exists. */
+int pkv_seqs_add(pkv_seqs *seqs, int64_t seq_id);
+/* New sequence whose first num_tokens positions share the physical blocks of
+ * sequence src_id (num_tokens a multiple of block_size and <= its length):
+ * the blocks gain a reference and are read-only for both. */
+int pkv_seqs_add_shared(pkv_seqs *seqs, int64_t seq_id, int64_t src_id, int32_t num_tokens);
+/* Extend a sequence by n tokens; slots[0..n) receive their slots.  New blocks
+ * come from the pool when a block boundary is crossed; all-or-nothing
+ * (PKV_ENOBLOCKS).  PKV_ESTATE if a slot would land in a block with
+ * refcount > 1. */
+int pkv_seqs_append(pkv_seqs *seqs, int64_t seq_id, int32_t n, int32_t *slots);
+/* One token for each of n sequences (a decode step); slots[i] for seq_ids[i].
+ * All-or-nothing across the batch. */
+int pkv_seqs_append_batch(pkv_seqs *seqs, int32_t n, const int64_t *seq_ids, int32_t *slots);
+/* Remove a sequence and drop its block references at once. */
+int pkv_seqs_release(pkv_seqs *seqs, int64_t seq_id);
+/* Length of a sequence, or -1 if unknown. */
+int32_t pkv_seqs_len(const pkv_seqs *seqs, int64_t seq_id);
+/* Copy up to cap block ids of a sequence into ids; returns the count, or a
+ * negative code. */
+int32_t pkv_seqs_block_ids(const pkv_seqs *seqs, int64_t seq_id, int32_t cap, int32_t *ids);
+/* Fill block_tables[i][0..stride) (padding -1) and context_lens[i] for the
+ * listed sequences, ready to copy to the device.  PKV_EINVAL if a sequence
+ * needs more than stride blocks. */
+int pkv_seqs_fill(const pkv_seqs *seqs, int32_t n, const int64_t *seq_ids,
+                  int32_t *block_tables, int32_t stride, int32_t *context_lens);
+int pkv_seqs_stats_get(const pkv_seqs *seqs, pkv_seqs_stats *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,386 @@
+"""Python binding of libpkv: paged-KV attention on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libpkv.so`` behind the C ABI declared in ``include/pkv.h``;
+torch supplies device memory and streams.  There is no fallback: if the
+library is not built, importing this package fails.
+
+Calls mirror the C ABI names: ``append`` (pkv_append), ``decode``
+(pkv_decode), ``prefill_chunk`` (pkv_prefill_chunk), ``Pool`` (pkv_pool_*)
+and ``Seqs`` (pkv_seqs_*).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_indirected_amd.build` "
+        "(no CPU fallback exists)")
+
+# One HIP runtime per process: torch ships its own libamdhip64, and a library
+# loaded before it would bind the system runtime instead, leaving two runtimes
+# that do not share devices, memory or streams.  Importing torch first makes
+# libpkv resolve the HIP runtime torch already loaded.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, EINVAL, EUNSUPPORTED, ENOBLOCKS, ESTATE, EHIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+
+_P = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_u64 = ctypes.c_uint64
+_sz = ctypes.c_size_t
+
+
+class CacheDescC(ctypes.Structure):
+    _fields_ = [("num_blocks", _i32), ("num_kv_heads", _i32), ("block_size", _i32),
+                ("head_dim", _i32), ("dtype", _i32)]
+
+
+class SeqsStatsC(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("blocks_referenced", _i64), ("blocks_in_use", _i32),
+                ("tokens", _i64), ("slots_unused", _i64)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_DESC = ctypes.POINTER(CacheDescC)
+_sig("pkv_strerror", ctypes.c_char_p, ctypes.c_int)
+_sig("pkv_last_error", ctypes.c_char_p)
+_sig("pkv_abi_version", ctypes.c_int)
+_sig("pkv_append", ctypes.c_int, _P, _P, _P, _i32, _P, _P, _DESC, _P)
+_sig("pkv_decode_partition_tokens", _i32, _i32, _i32, _i32, _DESC)
+_sig("pkv_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _DESC)
+_sig("pkv_decode", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, ctypes.c_float, _P,
+     _i32, _i32, _P, _sz, _DESC, _P)
+_sig("pkv_prefill_workspace_bytes", _sz, _i32, _i32, _i32, _DESC)
+_sig("pkv_prefill_chunk", ctypes.c_int, _P, _P, _i32, _i32, _P, _P, _P, _i32, _P, _i32, _i32,
+     ctypes.c_float, _P, _i32, _P, _sz, _DESC, _P)
+_sig("pkv_pool_create", _P, _i32, _u64)
+_sig("pkv_pool_destroy", None, _P)
+_sig("pkv_pool_alloc", ctypes.c_int, _P, _i32, _P)
+_sig("pkv_pool_share", ctypes.c_int, _P, _i32, _P)
+_sig("pkv_pool_release", ctypes.c_int, _P, _i32, _P)
+_sig("pkv_pool_num_free", _i32, _P)
+_sig("pkv_pool_num_blocks", _i32, _P)
+_sig("pkv_pool_refcount", _i32, _P, _i32)
+_sig("pkv_seqs_create", _P, _P, _i32)
+_sig("pkv_seqs_destroy", None, _P)
+_sig("pkv_seqs_add", ctypes.c_int, _P, _i64)
+_sig("pkv_seqs_add_shared", ctypes.c_int, _P, _i64, _i64, _i32)
+_sig("pkv_seqs_append", ctypes.c_int, _P, _i64, _i32, _P)
+_sig("pkv_seqs_append_batch", ctypes.c_int, _P, _i32, _P, _P)
+_sig("pkv_seqs_release", ctypes.c_int, _P, _i64)
+_sig("pkv_seqs_len", _i32, _P, _i64)
+_sig("pkv_seqs_block_ids", _i32, _P, _i64, _i32, _P)
+_sig("pkv_seqs_fill", ctypes.c_int, _P, _i32, _P, _P, _i32, _P)
+_sig("pkv_seqs_stats_get", ctypes.c_int, _P, ctypes.POINTER(SeqsStatsC))
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.pkv_last_error().decode() or _lib.pkv_strerror(code).decode()
+        super().__init__(f"{where}: {_lib.pkv_strerror(code).decode()} ({code}): {msg}")
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != OK:
+        raise PkvError(rc, where)
+
+
+def strerror(code: int) -> str:
+    return _lib.pkv_strerror(code).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.pkv_abi_version())
+
+
+@dataclass(frozen=True)
+class CacheDesc:
+    """Shape of one layer's cache: k_cache / v_cache are each
+    [num_blocks][num_kv_heads][block_size][head_dim] of ``dtype``."""
+    num_blocks: int
+    num_kv_heads: int
+    block_size: int
+    head_dim: int
+    dtype: int  # F32 or BF16
+
+    def c(self) -> CacheDescC:
+        return CacheDescC(self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim,
+                          self.dtype)
+
+    def cache_shape(self):
+        return (self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim)
+
+
+# ---------------------------------------------------------------------------
+# Tensor marshalling.
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name: str, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _need(cond: bool, what: str) -> None:
+    if not cond:
+        raise ValueError(what)
+
+
+def _cache_ok(t, desc: "CacheDesc", name: str) -> None:
+    _need(t.numel() == desc.num_blocks * desc.num_kv_heads * desc.block_size * desc.head_dim,
+          f"{name} does not match the cache descriptor {desc}")
+    _need(_dtype_code(t) == desc.dtype, f"{name} dtype does not match the descriptor")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def append(k, v, slot_mapping, k_cache, v_cache, desc: CacheDesc, stream=None) -> None:
+    """pkv_append: copy k/v rows ([T][Hkv][D]) into the cache slots
+    ``slot_mapping`` (int32 [T]; negative = skip)."""
+    torch = _torch()
+    T = int(slot_mapping.numel())
+    row = desc.num_kv_heads * desc.head_dim
+    _need(k.numel() == T * row and v.numel() == T * row, "k/v must be [T][Hkv][D]")
+    _need(_dtype_code(k) == desc.dtype and _dtype_code(v) == desc.dtype, "k/v dtype")
+    _cache_ok(k_cache, desc, "k_cache")
+    _cache_ok(v_cache, desc, "v_cache")
+    rc = _lib.pkv_append(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int32),
+                         T, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                         ctypes.byref(desc.c()), _stream(stream))
+    _check(rc, "pkv_append")
+
+
+def decode_partition_tokens(num_seqs: int, num_q_heads: int, max_context_len: int,
+                            desc: CacheDesc) -> int:
+    return int(_lib.pkv_decode_partition_tokens(num_seqs, num_q_heads, max_context_len,
+                                                ctypes.byref(desc.c())))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
+                           desc: CacheDesc, partition_tokens: int = 0) -> int:
+    return int(_lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                               partition_tokens, ctypes.byref(desc.c())))
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, desc: CacheDesc,
+           max_context_len: int, workspace=None, partition_tokens: int = 0, stream=None) -> None:
+    """pkv_decode: out[b][h] = softmax(scale q[b][h] K^T) V over the paged
+    context of sequence b.  ``workspace`` is a uint8 GPU tensor of at least
+    ``decode_workspace_bytes(...)`` bytes (None when that is 0)."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    _need(D == desc.head_dim and _dtype_code(q) == desc.dtype, "q must be [B][Hq][head_dim]")
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] >= B, "block_tables must be [B][W]")
+    _need(context_lens.numel() >= B, "context_lens must hold B entries")
+    _cache_ok(k_cache, desc, "k_cache")
+    _cache_ok(v_cache, desc, "v_cache")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.pkv_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                         _dev(block_tables, "block_tables", torch.int32),
+                         int(block_tables.shape[1]) if block_tables.dim() == 2 else 0,
+                         _dev(context_lens, "context_lens", torch.int32), B, Hq,
+                         int(max_context_len), float(scale), _dev(out, "out"), _dtype_code(out),
+                         int(partition_tokens), _dev(workspace, "workspace"), ws_bytes,
+                         ctypes.byref(desc.c()), _stream(stream))
+    _check(rc, "pkv_decode")
+
+
+def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, max_query_len: int,
+                            desc: CacheDesc) -> int:
+    return int(_lib.pkv_prefill_workspace_bytes(num_seqs, num_q_heads, max_query_len,
+                                                ctypes.byref(desc.c())))
+
+
+def prefill_chunk(q, query_start_loc, k_cache, v_cache, block_tables, context_lens, scale: float,
+                  out, desc: CacheDesc, max_query_len: int, max_context_len: int, workspace=None,
+                  stream=None) -> None:
+    """pkv_prefill_chunk: causal attention of each sequence's chunk rows over
+    its paged context (the chunk already appended)."""
+    torch = _torch()
+    S = int(query_start_loc.numel()) - 1
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim and _dtype_code(q) == desc.dtype,
+          "q must be [T][Hq][head_dim]")
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] >= S, "block_tables must be [S][W]")
+    _need(context_lens.numel() >= S, "context_lens must hold S entries")
+    _cache_ok(k_cache, desc, "k_cache")
+    _cache_ok(v_cache, desc, "v_cache")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.pkv_prefill_chunk(_dev(q, "q"), _dev(query_start_loc, "query_start_loc", torch.int32),
+                                S, int(max_query_len), _dev(k_cache, "k_cache"),
+                                _dev(v_cache, "v_cache"),
+                                _dev(block_tables, "block_tables", torch.int32),
+                                int(block_tables.shape[1]) if block_tables.dim() == 2 else 0,
+                                _dev(context_lens, "context_lens", torch.int32),
+                                int(max_context_len), int(q.shape[1]), float(scale),
+                                _dev(out, "out"), _dtype_code(out), _dev(workspace, "workspace"),
+                                ws_bytes, ctypes.byref(desc.c()), _stream(stream))
+    _check(rc, "pkv_prefill_chunk")
+
+
+# ---------------------------------------------------------------------------
+# Host pool and sequences.
+
+def _i32buf(n: int):
+    return (ctypes.c_int32 * max(n, 1))()
+
+
+class Pool:
+    """pkv_pool_*: physical block ids with reference counts."""
+
+    def __init__(self, num_blocks: int, seed: int = 0):
+        self._h = _lib.pkv_pool_create(int(num_blocks), int(seed) & (2**64 - 1))
+        if not self._h:
+            raise PkvError(EINVAL, "pkv_pool_create")
+
+    def close(self) -> None:
+        if self._h:
+            _lib.pkv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def alloc(self, n: int):
+        buf = _i32buf(n)
+        _check(_lib.pkv_pool_alloc(self._h, int(n), buf), "pkv_pool_alloc")
+        return list(buf[:n])
+
+    def share(self, ids: Sequence[int]) -> None:
+        buf = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        _check(_lib.pkv_pool_share(self._h, len(ids), buf), "pkv_pool_share")
+
+    def release(self, ids: Sequence[int]) -> None:
+        buf = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        _check(_lib.pkv_pool_release(self._h, len(ids), buf), "pkv_pool_release")
+
+    @property
+    def num_free(self) -> int:
+        return int(_lib.pkv_pool_num_free(self._h))
+
+    @property
+    def num_blocks(self) -> int:
+        return int(_lib.pkv_pool_num_blocks(self._h))
+
+    def refcount(self, block_id: int) -> int:
+        return int(_lib.pkv_pool_refcount(self._h, int(block_id)))
+
+
+class Seqs:
+    """pkv_seqs_*: per-sequence lengths and block lists over a Pool."""
+
+    def __init__(self, pool: Pool, block_size: int):
+        self.pool = pool  # keeps the pool alive
+        self.block_size = int(block_size)
+        self._h = _lib.pkv_seqs_create(pool.handle, int(block_size))
+        if not self._h:
+            raise PkvError(EINVAL, "pkv_seqs_create")
+
+    def close(self) -> None:
+        if self._h:
+            _lib.pkv_seqs_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add(self, seq_id: int) -> None:
+        _check(_lib.pkv_seqs_add(self._h, int(seq_id)), "pkv_seqs_add")
+
+    def add_shared(self, seq_id: int, src_id: int, num_tokens: int) -> None:
+        _check(_lib.pkv_seqs_add_shared(self._h, int(seq_id), int(src_id), int(num_tokens)),
+               "pkv_seqs_add_shared")
+
+    def append(self, seq_id: int, n: int):
+        """Extend by n tokens; returns their slots (a numpy int32 array)."""
+        import numpy as np
+        out = np.empty(max(int(n), 1), dtype=np.int32)
+        _check(_lib.pkv_seqs_append(self._h, int(seq_id), int(n), out.ctypes.data),
+               "pkv_seqs_append")
+        return out[:n]
+
+    def append_batch(self, seq_ids):
+        """One token for each listed sequence; returns the slots."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        out = np.empty(max(len(ids), 1), dtype=np.int32)
+        _check(_lib.pkv_seqs_append_batch(self._h, len(ids), ids.ctypes.data, out.ctypes.data),
+               "pkv_seqs_append_batch")
+        return out[:len(ids)]
+
+    def release(self, seq_id: int) -> None:
+        _check(_lib.pkv_seqs_release(self._h, int(seq_id)), "pkv_seqs_release")
+
+    def length(self, seq_id: int) -> int:
+        return int(_lib.pkv_seqs_len(self._h, int(seq_id)))
+
+    def block_ids(self, seq_id: int):
+        n = int(_lib.pkv_seqs_block_ids(self._h, int(seq_id), 0, None))
+        if n < 0:
+            raise PkvError(n, "pkv_seqs_block_ids")
+        buf = _i32buf(n)
+        _lib.pkv_seqs_block_ids(self._h, int(seq_id), n, buf)
+        return list(buf[:n])
+
+    def fill(self, seq_ids, stride: int):
+        """Block tables [n][stride] (padding -1) and context lengths [n], int32."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = np.empty((len(ids), int(stride)), dtype=np.int32)
+        lens = np.empty(max(len(ids), 1), dtype=np.int32)
+        _check(_lib.pkv_seqs_fill(self._h, len(ids), ids.ctypes.data, tables.ctypes.data,
+                                  int(stride), lens.ctypes.data), "pkv_seqs_fill")
+        return tables, lens[:len(ids)]
+
+    def stats(self) -> dict:
+        st = SeqsStatsC()
+        _check(_lib.pkv_seqs_stats_get(self._h, ctypes.byref(st)), "pkv_seqs_stats_get")
+        return {f: getattr(st, f) for f, _ in SeqsStatsC._fields_}

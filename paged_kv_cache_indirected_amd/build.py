@@ -1,0 +1,70 @@
+"""Build libpkv.so (HIP kernels for gfx950 + host C++), in-tree.
+
+    python -m paged_kv_cache_indirected_amd.build
+
+Host translation units are compiled by g++, HIP ones by hipcc for gfx950
+only, then linked with hipcc into the package directory.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpkv.so")
+OBJ = os.path.join(ROOT, "_build", "pkv")
+
+HOST_SRC = ["errors.cpp", "pool.cpp", "api.cpp"]
+HIP_SRC = ["append.hip", "decode.hip", "prefill.hip"]
+
+ARCH = "gfx950"
+# Packed fp32 vector ops are switched off for all device code.
+HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-I" + INCLUDE,
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I" + INCLUDE]
+
+
+def _hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    hipcc = _hipcc()
+    jobs = []
+    for s in HOST_SRC:
+        jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, s), "-o",
+                     os.path.join(OBJ, s + ".o")])
+    for s in HIP_SRC:
+        jobs.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, s), "-o",
+                     os.path.join(OBJ, s + ".o")])
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        for r in ex.map(_run, jobs):
+            if verbose and (r.stdout or r.stderr):
+                print(r.stdout, r.stderr, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    objs = [os.path.join(OBJ, s + ".o") for s in HOST_SRC + HIP_SRC]
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,255 @@
+// C ABI entry points of libpkv: argument validation, launch geometry and
+// workspace sizing.  Every step of the computation runs in the HIP kernels;
+// this file only checks host scalars and pointers and picks launch shapes.
+#include <cmath>
+
+#include "pkv_internal.h"
+
+using pkv::fail;
+
+namespace {
+
+constexpr int kWavesPerGroup = 4;   // decode workgroup: 4 waves, each takes every 4th block
+
+int check_desc(const pkv_cache_desc *c, const char *who)
+{
+    if (!c)
+        return fail(PKV_EINVAL, "%s: null cache descriptor", who);
+    if (c->num_blocks <= 0 || c->num_kv_heads <= 0)
+        return fail(PKV_EINVAL, "%s: num_blocks %d and num_kv_heads %d must be positive", who,
+                    c->num_blocks, c->num_kv_heads);
+    if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
+        return fail(PKV_EUNSUPPORTED, "%s: dtype %d", who, c->dtype);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(PKV_EUNSUPPORTED, "%s: head_dim %d (64 or 128)", who, c->head_dim);
+    if (c->block_size != 16 && c->block_size != 32)
+        return fail(PKV_EUNSUPPORTED, "%s: block_size %d (16 or 32)", who, c->block_size);
+    if ((int64_t)c->num_blocks * c->block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "%s: num_blocks * block_size exceeds int32 slots", who);
+    return PKV_OK;
+}
+
+int elem_size(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+int check_ptr(const void *p, const char *what, const char *who)
+{
+    if (!p)
+        return fail(PKV_EINVAL, "%s: %s is NULL", who, what);
+    if (!pkv::aligned16(p))
+        return fail(PKV_EINVAL, "%s: %s is not 16-byte aligned", who, what);
+    return PKV_OK;
+}
+
+int check_heads(int32_t hq, const pkv_cache_desc *c, const char *who)
+{
+    if (hq <= 0 || hq % c->num_kv_heads != 0)
+        return fail(PKV_EINVAL, "%s: num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                    who, hq, c->num_kv_heads);
+    const int32_t G = hq / c->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(PKV_EUNSUPPORTED, "%s: query group %d (1, 2, 4 or 8)", who, G);
+    return PKV_OK;
+}
+
+// Partition size: the largest power-of-two multiple of 4 blocks, at most 2048
+// tokens, that still gives at least 2048 workgroups (8 per CU on 256 CUs) for
+// the (sequence, KV head) pairs at the longest context.
+int32_t auto_partition_tokens(int32_t num_seqs, int32_t max_ctx, const pkv_cache_desc *c)
+{
+    const int32_t unit = kWavesPerGroup * c->block_size;
+    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads;
+    const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
+    int32_t pt = 2048;
+    while (pt > unit && pairs * ((ctx + pt - 1) / pt) < 2048)
+        pt /= 2;
+    return pt < unit ? unit : pt;
+}
+
+int32_t max_partitions(int32_t max_ctx, int32_t pt)
+{
+    const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
+    return (int32_t)((ctx + pt - 1) / pt);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Bytes of the split partials: o [B][Hq][P][D] then (m, l) [B][Hq][P][2], fp32.
+size_t ws_bytes(int32_t B, int32_t hq, int32_t P, int32_t D)
+{
+    if (P <= 1 || B <= 0)
+        return 0;
+    const size_t rows = (size_t)B * hq * P;
+    return align256(rows * D * sizeof(float)) + rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" int pkv_append(const void *k, const void *v, const int32_t *slot_mapping,
+                          int32_t num_tokens, void *k_cache, void *v_cache,
+                          const pkv_cache_desc *c, void *stream)
+{
+    static const char *who = "pkv_append";
+    pkv::clear_error();
+    int rc = check_desc(c, who);
+    if (rc)
+        return rc;
+    if (num_tokens < 0)
+        return fail(PKV_EINVAL, "%s: num_tokens %d", who, num_tokens);
+    if (num_tokens == 0)
+        return PKV_OK;
+    if ((rc = check_ptr(k, "k", who)) || (rc = check_ptr(v, "v", who)) ||
+        (rc = check_ptr(k_cache, "k_cache", who)) || (rc = check_ptr(v_cache, "v_cache", who)))
+        return rc;
+    if (!slot_mapping)
+        return fail(PKV_EINVAL, "%s: slot_mapping is NULL", who);
+    pkv::AppendLaunch a{k, v, slot_mapping, num_tokens, k_cache, v_cache, c->num_blocks,
+                        c->num_kv_heads, c->block_size, c->head_dim, elem_size(c->dtype), stream};
+    return pkv::launch_append(a);
+}
+
+extern "C" int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t max_context_len, const pkv_cache_desc *c)
+{
+    (void)num_q_heads;
+    if (check_desc(c, "pkv_decode_partition_tokens"))
+        return 0;
+    return auto_partition_tokens(num_seqs, max_context_len, c);
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t max_context_len, int32_t partition_tokens,
+                                             const pkv_cache_desc *c)
+{
+    if (check_desc(c, "pkv_decode_workspace_bytes") || num_seqs < 0 || num_q_heads <= 0)
+        return 0;
+    const int32_t pt = partition_tokens > 0 ? partition_tokens
+                                            : auto_partition_tokens(num_seqs, max_context_len, c);
+    return ws_bytes(num_seqs, num_q_heads, max_partitions(max_context_len, pt), c->head_dim);
+}
+
+extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_tables, int32_t block_table_stride,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+                          int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                          const pkv_cache_desc *c, void *stream)
+{
+    static const char *who = "pkv_decode";
+    pkv::clear_error();
+    int rc = check_desc(c, who);
+    if (rc || (rc = check_heads(num_q_heads, c, who)))
+        return rc;
+    if (num_seqs < 0 || num_seqs > 65535)
+        return fail(PKV_EINVAL, "%s: num_seqs %d (0 .. 65535)", who, num_seqs);
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
+        return fail(PKV_EINVAL, "%s: out_dtype %d", who, out_dtype);
+    if (!std::isfinite(scale))
+        return fail(PKV_EINVAL, "%s: scale is not finite", who);
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (block_table_stride <= 0 || max_context_len < 0 ||
+        (int64_t)max_context_len > (int64_t)block_table_stride * c->block_size)
+        return fail(PKV_EINVAL,
+                    "%s: max_context_len %d must lie in [0, block_table_stride %d * block_size]",
+                    who, max_context_len, block_table_stride);
+    const int32_t unit = kWavesPerGroup * c->block_size;
+    if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % unit != 0))
+        return fail(PKV_EINVAL, "%s: partition_tokens %d must be 0 or a multiple of %d", who,
+                    partition_tokens, unit);
+    if ((rc = check_ptr(q, "q", who)) || (rc = check_ptr(k_cache, "k_cache", who)) ||
+        (rc = check_ptr(v_cache, "v_cache", who)) || (rc = check_ptr(out, "out", who)))
+        return rc;
+    if (!block_tables || !context_lens)
+        return fail(PKV_EINVAL, "%s: block_tables or context_lens is NULL", who);
+    const int32_t pt = partition_tokens > 0 ? partition_tokens
+                                            : auto_partition_tokens(num_seqs, max_context_len, c);
+    const int32_t P = max_partitions(max_context_len, pt);
+    if (P > 65535)
+        return fail(PKV_EINVAL, "%s: %d partitions exceed the grid", who, P);
+    const size_t need = ws_bytes(num_seqs, num_q_heads, P, c->head_dim);
+    if (need > 0) {
+        if ((rc = check_ptr(workspace, "workspace", who)))
+            return rc;
+        if (workspace_bytes < need)
+            return fail(PKV_EINVAL, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                        need);
+    }
+    pkv::DecodeLaunch d{};
+    d.q = q;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.block_tables = block_tables;
+    d.table_stride = block_table_stride;
+    d.context_lens = context_lens;
+    d.num_seqs = num_seqs;
+    d.num_q_heads = num_q_heads;
+    d.num_kv_heads = c->num_kv_heads;
+    d.num_blocks = c->num_blocks;
+    d.block_size = c->block_size;
+    d.head_dim = c->head_dim;
+    d.dtype = c->dtype;
+    d.partition_blocks = pt / c->block_size;
+    d.max_partitions = P;
+    d.scale = scale;
+    d.out = out;
+    d.out_dtype = out_dtype;
+    if (need > 0) {
+        const size_t rows = (size_t)num_seqs * num_q_heads * P;
+        d.ws_o = static_cast<float *>(workspace);
+        d.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                            align256(rows * c->head_dim * sizeof(float)));
+    }
+    d.stream = stream;
+    return pkv::launch_decode(d);
+}
+
+extern "C" size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t max_query_len, const pkv_cache_desc *c)
+{
+    (void)num_seqs;
+    (void)num_q_heads;
+    (void)max_query_len;
+    (void)c;
+    return 0;
+}
+
+extern "C" int pkv_prefill_chunk(const void *q, const int32_t *query_start_loc, int32_t num_seqs,
+                                 int32_t max_query_len, const void *k_cache, const void *v_cache,
+                                 const int32_t *block_tables, int32_t block_table_stride,
+                                 const int32_t *context_lens, int32_t max_context_len,
+                                 int32_t num_q_heads, float scale, void *out, int32_t out_dtype,
+                                 void *workspace, size_t workspace_bytes, const pkv_cache_desc *c,
+                                 void *stream)
+{
+    static const char *who = "pkv_prefill_chunk";
+    (void)workspace;
+    (void)workspace_bytes;
+    pkv::clear_error();
+    int rc = check_desc(c, who);
+    if (rc || (rc = check_heads(num_q_heads, c, who)))
+        return rc;
+    if (c->dtype != PKV_BF16)
+        return fail(PKV_EUNSUPPORTED, "%s: the MFMA path takes bf16 only", who);
+    if (num_seqs < 0 || num_seqs > 65535)
+        return fail(PKV_EINVAL, "%s: num_seqs %d (0 .. 65535)", who, num_seqs);
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
+        return fail(PKV_EINVAL, "%s: out_dtype %d", who, out_dtype);
+    if (!std::isfinite(scale))
+        return fail(PKV_EINVAL, "%s: scale is not finite", who);
+    if (num_seqs == 0 || max_query_len == 0)
+        return PKV_OK;
+    if (max_query_len < 0 || block_table_stride <= 0 || max_context_len < 0 ||
+        (int64_t)max_context_len > (int64_t)block_table_stride * c->block_size)
+        return fail(PKV_EINVAL, "%s: bad max_query_len %d / max_context_len %d / stride %d", who,
+                    max_query_len, max_context_len, block_table_stride);
+    if ((rc = check_ptr(q, "q", who)) || (rc = check_ptr(k_cache, "k_cache", who)) ||
+        (rc = check_ptr(v_cache, "v_cache", who)) || (rc = check_ptr(out, "out", who)))
+        return rc;
+    if (!query_start_loc || !block_tables || !context_lens)
+        return fail(PKV_EINVAL, "%s: query_start_loc, block_tables or context_lens is NULL", who);
+    pkv::PrefillLaunch p{q, query_start_loc, num_seqs, max_query_len, k_cache, v_cache,
+                         block_tables, block_table_stride, context_lens, max_context_len,
+                         num_q_heads, c->num_kv_heads, c->num_blocks, c->block_size, c->head_dim,
+                         scale, out, out_dtype, stream};
+    return pkv::launch_prefill(p);
+}

@@ -1,0 +1,361 @@
+// Host-side block pool and sequence bookkeeping.
+//
+// Follows "LLM Inference: KV Cache, Batching & Scheduling", section
+// "PagedAttention and vLLM": KV lives in fixed-size blocks, pages are
+// allocated on demand and a finished request's pages return to the pool at
+// once; and the "LLM Inference Engineering" summary, section 2, with the
+// blog post's "The Elegant Fix": sequences with an identical prefix share its
+// pages.  Sharing is reference counted; a shared block is read-only.
+//
+// Single-threaded by contract (one scheduler thread owns a pool).
+#include <algorithm>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv_internal.h"
+
+using pkv::fail;
+
+struct pkv_pool {
+    int32_t num_blocks = 0;
+    std::vector<int32_t> ref;     // refcount per block, 0 = free
+    std::deque<int32_t> free_q;   // front is handed out next; released blocks go to the back
+};
+
+namespace {
+
+// splitmix64: a small, well-known 64-bit mixing generator (Steele, Lea and
+// Flood, 2014) used only to draw the initial free-list order.
+uint64_t splitmix64(uint64_t &s)
+{
+    uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+bool valid_id(const pkv_pool *p, int32_t id) { return id >= 0 && id < p->num_blocks; }
+
+}  // namespace
+
+extern "C" pkv_pool *pkv_pool_create(int32_t num_blocks, uint64_t seed)
+{
+    if (num_blocks <= 0) {
+        fail(PKV_EINVAL, "pkv_pool_create: num_blocks must be positive (got %d)", num_blocks);
+        return nullptr;
+    }
+    pkv_pool *p = new (std::nothrow) pkv_pool;
+    if (!p)
+        return nullptr;
+    try {
+        p->num_blocks = num_blocks;
+        p->ref.assign(num_blocks, 0);
+        std::vector<int32_t> order(num_blocks);
+        for (int32_t i = 0; i < num_blocks; ++i)
+            order[i] = i;
+        if (seed != 0) {
+            // Fisher-Yates with an unbiased bounded draw (rejection sampling).
+            uint64_t s = seed;
+            for (int32_t i = num_blocks - 1; i > 0; --i) {
+                uint64_t bound = (uint64_t)i + 1, lim = UINT64_MAX - UINT64_MAX % bound, x;
+                do {
+                    x = splitmix64(s);
+                } while (x >= lim);
+                std::swap(order[i], order[(size_t)(x % bound)]);
+            }
+        }
+        p->free_q.assign(order.begin(), order.end());
+    } catch (...) {
+        delete p;
+        return nullptr;
+    }
+    return p;
+}
+
+extern "C" void pkv_pool_destroy(pkv_pool *pool) { delete pool; }
+
+extern "C" int pkv_pool_alloc(pkv_pool *p, int32_t n, int32_t *ids)
+{
+    if (!p || n < 0 || (n > 0 && !ids))
+        return fail(PKV_EINVAL, "pkv_pool_alloc: bad arguments");
+    if ((size_t)n > p->free_q.size())
+        return fail(PKV_ENOBLOCKS, "pkv_pool_alloc: %d blocks requested, %zu free", n,
+                    p->free_q.size());
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t id = p->free_q.front();
+        p->free_q.pop_front();
+        p->ref[id] = 1;
+        ids[i] = id;
+    }
+    return PKV_OK;
+}
+
+extern "C" int pkv_pool_share(pkv_pool *p, int32_t n, const int32_t *ids)
+{
+    if (!p || n < 0 || (n > 0 && !ids))
+        return fail(PKV_EINVAL, "pkv_pool_share: bad arguments");
+    for (int32_t i = 0; i < n; ++i)
+        if (!valid_id(p, ids[i]) || p->ref[ids[i]] == 0)
+            return fail(PKV_ESTATE, "pkv_pool_share: block %d is free or unknown", ids[i]);
+    for (int32_t i = 0; i < n; ++i)
+        ++p->ref[ids[i]];
+    return PKV_OK;
+}
+
+extern "C" int pkv_pool_release(pkv_pool *p, int32_t n, const int32_t *ids)
+{
+    if (!p || n < 0 || (n > 0 && !ids))
+        return fail(PKV_EINVAL, "pkv_pool_release: bad arguments");
+    std::unordered_map<int32_t, int32_t> count;
+    for (int32_t i = 0; i < n; ++i) {
+        if (!valid_id(p, ids[i]))
+            return fail(PKV_ESTATE, "pkv_pool_release: unknown block %d", ids[i]);
+        if (++count[ids[i]] > p->ref[ids[i]])
+            return fail(PKV_ESTATE, "pkv_pool_release: block %d released more often than held",
+                        ids[i]);
+    }
+    for (int32_t i = 0; i < n; ++i)
+        if (--p->ref[ids[i]] == 0)
+            p->free_q.push_back(ids[i]);
+    return PKV_OK;
+}
+
+extern "C" int32_t pkv_pool_num_free(const pkv_pool *p) { return p ? (int32_t)p->free_q.size() : -1; }
+
+extern "C" int32_t pkv_pool_num_blocks(const pkv_pool *p) { return p ? p->num_blocks : -1; }
+
+extern "C" int32_t pkv_pool_refcount(const pkv_pool *p, int32_t id)
+{
+    return (p && valid_id(p, id)) ? p->ref[id] : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Sequences.
+
+namespace {
+struct Seq {
+    int32_t len = 0;
+    std::vector<int32_t> blocks;
+};
+}  // namespace
+
+struct pkv_seqs {
+    pkv_pool *pool = nullptr;
+    int32_t bs = 0;
+    std::unordered_map<int64_t, Seq> seqs;
+};
+
+extern "C" pkv_seqs *pkv_seqs_create(pkv_pool *pool, int32_t block_size)
+{
+    if (!pool || block_size <= 0) {
+        fail(PKV_EINVAL, "pkv_seqs_create: bad arguments");
+        return nullptr;
+    }
+    pkv_seqs *s = new (std::nothrow) pkv_seqs;
+    if (!s)
+        return nullptr;
+    s->pool = pool;
+    s->bs = block_size;
+    return s;
+}
+
+extern "C" void pkv_seqs_destroy(pkv_seqs *s) { delete s; }
+
+extern "C" int pkv_seqs_add(pkv_seqs *s, int64_t id)
+{
+    if (!s)
+        return fail(PKV_EINVAL, "pkv_seqs_add: null handle");
+    if (s->seqs.count(id))
+        return fail(PKV_ESTATE, "pkv_seqs_add: sequence %lld exists", (long long)id);
+    s->seqs.emplace(id, Seq{});
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_add_shared(pkv_seqs *s, int64_t id, int64_t src, int32_t num_tokens)
+{
+    if (!s)
+        return fail(PKV_EINVAL, "pkv_seqs_add_shared: null handle");
+    auto it = s->seqs.find(src);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_add_shared: unknown source %lld", (long long)src);
+    if (s->seqs.count(id))
+        return fail(PKV_ESTATE, "pkv_seqs_add_shared: sequence %lld exists", (long long)id);
+    if (num_tokens < 0 || num_tokens % s->bs != 0 || num_tokens > it->second.len)
+        return fail(PKV_EINVAL,
+                    "pkv_seqs_add_shared: %d tokens is not a whole-block prefix of a %d-token "
+                    "sequence",
+                    num_tokens, it->second.len);
+    Seq n;
+    n.len = num_tokens;
+    n.blocks.assign(it->second.blocks.begin(), it->second.blocks.begin() + num_tokens / s->bs);
+    int rc = pkv_pool_share(s->pool, (int32_t)n.blocks.size(), n.blocks.data());
+    if (rc != PKV_OK)
+        return rc;
+    s->seqs.emplace(id, std::move(n));
+    return PKV_OK;
+}
+
+namespace {
+
+// Blocks a sequence of `len` tokens must gain to hold `len + n`.
+int32_t blocks_needed(const Seq &q, int32_t bs, int32_t n)
+{
+    int64_t need = ((int64_t)q.len + n + bs - 1) / bs;
+    return (int32_t)std::max<int64_t>(0, need - (int64_t)q.blocks.size());
+}
+
+// Appending into the partially filled last block is only allowed when that
+// block is private.
+bool writes_shared_block(const pkv_seqs *s, const Seq &q, int32_t n)
+{
+    if (n <= 0 || q.len % s->bs == 0 || q.blocks.empty())
+        return false;
+    return pkv_pool_refcount(s->pool, q.blocks.back()) > 1;
+}
+
+void take_slots(const pkv_seqs *s, Seq &q, int32_t n, int32_t *slots)
+{
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t pos = q.len + i;
+        slots[i] = q.blocks[pos / s->bs] * s->bs + pos % s->bs;
+    }
+    q.len += n;
+}
+
+}  // namespace
+
+extern "C" int pkv_seqs_append(pkv_seqs *s, int64_t id, int32_t n, int32_t *slots)
+{
+    if (!s || n < 0 || (n > 0 && !slots))
+        return fail(PKV_EINVAL, "pkv_seqs_append: bad arguments");
+    auto it = s->seqs.find(id);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_append: unknown sequence %lld", (long long)id);
+    Seq &q = it->second;
+    if ((int64_t)q.len + n > INT32_MAX / 2)
+        return fail(PKV_EINVAL, "pkv_seqs_append: sequence too long");
+    if (writes_shared_block(s, q, n))
+        return fail(PKV_ESTATE, "pkv_seqs_append: sequence %lld would write into a shared block",
+                    (long long)id);
+    int32_t nb = blocks_needed(q, s->bs, n);
+    std::vector<int32_t> fresh(nb);
+    int rc = pkv_pool_alloc(s->pool, nb, fresh.data());
+    if (rc != PKV_OK)
+        return rc;
+    q.blocks.insert(q.blocks.end(), fresh.begin(), fresh.end());
+    take_slots(s, q, n, slots);
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_append_batch(pkv_seqs *s, int32_t n, const int64_t *ids, int32_t *slots)
+{
+    if (!s || n < 0 || (n > 0 && (!ids || !slots)))
+        return fail(PKV_EINVAL, "pkv_seqs_append_batch: bad arguments");
+    std::vector<Seq *> qs(n);
+    int32_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = s->seqs.find(ids[i]);
+        if (it == s->seqs.end())
+            return fail(PKV_ESTATE, "pkv_seqs_append_batch: unknown sequence %lld",
+                        (long long)ids[i]);
+        for (int32_t j = 0; j < i; ++j)
+            if (ids[j] == ids[i])
+                return fail(PKV_EINVAL, "pkv_seqs_append_batch: sequence %lld listed twice",
+                            (long long)ids[i]);
+        qs[i] = &it->second;
+        if (writes_shared_block(s, *qs[i], 1))
+            return fail(PKV_ESTATE,
+                        "pkv_seqs_append_batch: sequence %lld would write into a shared block",
+                        (long long)ids[i]);
+        total += blocks_needed(*qs[i], s->bs, 1);
+    }
+    std::vector<int32_t> fresh(total);
+    int rc = pkv_pool_alloc(s->pool, total, fresh.data());
+    if (rc != PKV_OK)
+        return rc;
+    int32_t k = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (blocks_needed(*qs[i], s->bs, 1))
+            qs[i]->blocks.push_back(fresh[k++]);
+        take_slots(s, *qs[i], 1, slots + i);
+    }
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_release(pkv_seqs *s, int64_t id)
+{
+    if (!s)
+        return fail(PKV_EINVAL, "pkv_seqs_release: null handle");
+    auto it = s->seqs.find(id);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_release: unknown sequence %lld", (long long)id);
+    int rc = pkv_pool_release(s->pool, (int32_t)it->second.blocks.size(), it->second.blocks.data());
+    if (rc != PKV_OK)
+        return rc;
+    s->seqs.erase(it);
+    return PKV_OK;
+}
+
+extern "C" int32_t pkv_seqs_len(const pkv_seqs *s, int64_t id)
+{
+    if (!s)
+        return -1;
+    auto it = s->seqs.find(id);
+    return it == s->seqs.end() ? -1 : it->second.len;
+}
+
+extern "C" int32_t pkv_seqs_block_ids(const pkv_seqs *s, int64_t id, int32_t cap, int32_t *ids)
+{
+    if (!s || cap < 0 || (cap > 0 && !ids))
+        return fail(PKV_EINVAL, "pkv_seqs_block_ids: bad arguments");
+    auto it = s->seqs.find(id);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_block_ids: unknown sequence %lld", (long long)id);
+    const auto &b = it->second.blocks;
+    int32_t n = std::min<int32_t>(cap, (int32_t)b.size());
+    if (n > 0)
+        std::memcpy(ids, b.data(), sizeof(int32_t) * n);
+    return (int32_t)b.size();
+}
+
+extern "C" int pkv_seqs_fill(const pkv_seqs *s, int32_t n, const int64_t *ids, int32_t *tables,
+                             int32_t stride, int32_t *lens)
+{
+    if (!s || n < 0 || stride <= 0 || (n > 0 && (!ids || !tables || !lens)))
+        return fail(PKV_EINVAL, "pkv_seqs_fill: bad arguments");
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = s->seqs.find(ids[i]);
+        if (it == s->seqs.end())
+            return fail(PKV_ESTATE, "pkv_seqs_fill: unknown sequence %lld", (long long)ids[i]);
+        if ((int64_t)it->second.blocks.size() > stride)
+            return fail(PKV_EINVAL, "pkv_seqs_fill: sequence %lld has %zu blocks > stride %d",
+                        (long long)ids[i], it->second.blocks.size(), stride);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq &q = s->seqs.find(ids[i])->second;
+        int32_t *row = tables + (int64_t)i * stride;
+        std::fill(row, row + stride, -1);
+        std::copy(q.blocks.begin(), q.blocks.end(), row);
+        lens[i] = q.len;
+    }
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_stats_get(const pkv_seqs *s, pkv_seqs_stats *out)
+{
+    if (!s || !out)
+        return fail(PKV_EINVAL, "pkv_seqs_stats_get: bad arguments");
+    pkv_seqs_stats st{};
+    st.num_seqs = (int32_t)s->seqs.size();
+    for (const auto &kv : s->seqs) {
+        st.blocks_referenced += (int64_t)kv.second.blocks.size();
+        st.tokens += kv.second.len;
+        st.slots_unused += (int64_t)kv.second.blocks.size() * s->bs - kv.second.len;
+    }
+    st.blocks_in_use = pkv_pool_num_blocks(s->pool) - pkv_pool_num_free(s->pool);
+    *out = st;
+    return PKV_OK;
+}

@@ -1,0 +1,107 @@
+"""Paged-cache state on the GPU, driven only through the libpkv C ABI.
+
+``PagedCache`` owns one layer's k_cache / v_cache tensors, a host block
+pool and the sequence bookkeeping, and loads K/V rows into the cache with
+``pkv_append`` at the slots the pool hands out.  It is the host side of a
+serving step ("LLM Inference: KV Cache, Batching & Scheduling", sections
+"PagedAttention and vLLM" and "Continuous batching (Orca)"): sequences are
+added, grow by appends, share whole prefix blocks, and are released, their
+blocks returning to the pool at once.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional
+
+import numpy as np
+import torch
+
+from . import BF16, F32, CacheDesc, Pool, Seqs, append
+
+# Quiet-NaN bit patterns written into every cache element before any append,
+# so a read of an unused slot or block would surface in the output.
+POISON_BITS = {F32: 0x7FC00000, BF16: 0x7FC0}
+
+
+def torch_dtype(code: int):
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+def to_device_rows(rows: np.ndarray, code: int, device) -> torch.Tensor:
+    """Host rows (float32, or bf16 bit patterns as uint16) -> device tensor."""
+    if code == F32:
+        t = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.float32))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.uint16).view(np.int16))
+        t = t.view(torch.bfloat16)
+    return t.to(device, non_blocking=False)
+
+
+class PagedCache:
+    """One layer's paged K/V cache plus its host-side block bookkeeping."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                 dtype: int, device="cuda", pool_seed: int = 0, poison: Optional[int] = None):
+        self.desc = CacheDesc(int(num_blocks), int(num_kv_heads), int(block_size), int(head_dim),
+                              int(dtype))
+        self.device = torch.device(device)
+        shape = self.desc.cache_shape()
+        bits = POISON_BITS[dtype] if poison is None else poison
+        if dtype == F32:
+            fill = torch.tensor(bits, dtype=torch.int64).to(torch.int32)
+            self.k_cache = torch.full(shape, int(fill), dtype=torch.int32, device=self.device)
+            self.k_cache = self.k_cache.view(torch.float32)
+        else:
+            v16 = bits - 0x10000 if bits >= 0x8000 else bits
+            self.k_cache = torch.full(shape, v16, dtype=torch.int16, device=self.device)
+            self.k_cache = self.k_cache.view(torch.bfloat16)
+        self.v_cache = self.k_cache.clone()
+        self.pool = Pool(num_blocks, pool_seed)
+        self.seqs = Seqs(self.pool, block_size)
+        self.stream = None
+
+    @property
+    def dtype(self) -> int:
+        return self.desc.dtype
+
+    def write(self, slots: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray) -> None:
+        """pkv_append of host rows [T][Hkv][D] into the given slots."""
+        if len(slots) == 0:
+            return
+        s = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).to(self.device)
+        k = to_device_rows(k_rows, self.dtype, self.device)
+        v = to_device_rows(v_rows, self.dtype, self.device)
+        append(k, v, s, self.k_cache, self.v_cache, self.desc)
+
+    def add_sequences(self, seq_ids: Iterable[int], lens, k_rows: np.ndarray,
+                      v_rows: np.ndarray) -> np.ndarray:
+        """Add sequences holding lens[i] rows each (rows concatenated in
+        k_rows / v_rows); returns the slots the rows were written to."""
+        slots = []
+        for sid, L in zip(seq_ids, lens):
+            self.seqs.add(int(sid))
+            slots.append(self.seqs.append(int(sid), int(L)))
+        slots = np.concatenate(slots) if slots else np.zeros(0, dtype=np.int32)
+        self.write(slots, k_rows, v_rows)
+        return slots
+
+    def add_shared(self, seq_id: int, src_id: int, num_tokens: int) -> None:
+        self.seqs.add_shared(int(seq_id), int(src_id), int(num_tokens))
+
+    def extend(self, seq_id: int, k_rows: np.ndarray, v_rows: np.ndarray) -> np.ndarray:
+        slots = self.seqs.append(int(seq_id), len(k_rows))
+        self.write(slots, k_rows, v_rows)
+        return slots
+
+    def release(self, seq_id: int) -> None:
+        self.seqs.release(int(seq_id))
+
+    def tables(self, seq_ids, stride: Optional[int] = None):
+        """Device block tables [n][stride] and context lengths [n] (int32),
+        and the host maximum length."""
+        ids = list(seq_ids)
+        if stride is None:
+            stride = max(1, max((len(self.seqs.block_ids(i)) for i in ids), default=1))
+        tab, lens = self.seqs.fill(ids, stride)
+        max_len = int(lens.max()) if len(lens) else 0
+        return (torch.from_numpy(tab).to(self.device), torch.from_numpy(lens.copy()).to(self.device),
+                max_len)

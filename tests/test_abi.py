@@ -1,0 +1,135 @@
+"""The C ABI library loads, exports every symbol include/pkv.h declares, and
+rejects bad host arguments before any launch (CPU only: no kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_indirected_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert "pkv_decode" in names and "pkv_append" in names and "pkv_prefill_chunk" in names
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_strerror():
+    assert pkv.abi_version() == 1
+    for code in (pkv.OK, pkv.EINVAL, pkv.EUNSUPPORTED, pkv.ENOBLOCKS, pkv.ESTATE, pkv.EHIP):
+        assert pkv.strerror(code) and pkv.strerror(code) != "unknown error code"
+
+
+L = pkv._lib
+FAKE = 0x10000          # a 16-byte aligned address that is never dereferenced
+MIS = 0x10004
+
+
+def _desc(**kw):
+    d = dict(num_blocks=64, num_kv_heads=8, block_size=16, head_dim=128, dtype=pkv.BF16)
+    d.update(kw)
+    return pkv.CacheDescC(**d)
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, stride=8, lens=FAKE, B=2, Hq=64, maxL=100,
+             scale=0.1, out=FAKE, odt=pkv.F32, pt=0, ws=FAKE, wsb=1 << 30, desc=_desc())
+    a.update(kw)
+    return L.pkv_decode(a["q"], a["kc"], a["vc"], a["bt"], a["stride"], a["lens"], a["B"], a["Hq"],
+                        a["maxL"], a["scale"], a["out"], a["odt"], a["pt"], a["ws"], a["wsb"],
+                        ctypes.byref(a["desc"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), pkv.EINVAL),
+    (dict(q=MIS), pkv.EINVAL),
+    (dict(out=None), pkv.EINVAL),
+    (dict(Hq=60), pkv.EINVAL),
+    (dict(Hq=128), pkv.EUNSUPPORTED),          # group of 16
+    (dict(desc=_desc(head_dim=96)), pkv.EUNSUPPORTED),
+    (dict(desc=_desc(block_size=8)), pkv.EUNSUPPORTED),
+    (dict(desc=_desc(dtype=7)), pkv.EUNSUPPORTED),
+    (dict(desc=_desc(num_blocks=0)), pkv.EINVAL),
+    (dict(maxL=16 * 8 + 1), pkv.EINVAL),       # beyond stride * block_size
+    (dict(pt=48), pkv.EINVAL),                 # not a multiple of 4 blocks
+    (dict(odt=3), pkv.EINVAL),
+    (dict(scale=float("nan")), pkv.EINVAL),
+    (dict(B=-1), pkv.EINVAL),
+    (dict(maxL=128, pt=64, wsb=16), pkv.EINVAL),   # short workspace
+    (dict(maxL=128, pt=64, ws=None), pkv.EINVAL),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+    assert pkv._lib.pkv_last_error().decode() != ""
+
+
+def test_decode_empty_batch_is_a_noop():
+    assert _decode(B=0, q=None, out=None) == pkv.OK
+
+
+def test_workspace_size_rules():
+    d = _desc()
+    # One partition per sequence needs no workspace.
+    assert L.pkv_decode_workspace_bytes(4, 64, 256, 256, ctypes.byref(d)) == 0
+    n = L.pkv_decode_workspace_bytes(4, 64, 1000, 256, ctypes.byref(d))
+    P = (1000 + 255) // 256
+    rows = 4 * 64 * P
+    assert n >= rows * 128 * 4 + rows * 2 * 4
+    pt = L.pkv_decode_partition_tokens(32, 64, 4096, ctypes.byref(d))
+    assert pt > 0 and pt % (4 * 16) == 0
+
+
+def test_append_rejects():
+    d = _desc()
+    assert L.pkv_append(None, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(d), None) == pkv.EINVAL
+    assert L.pkv_append(FAKE, FAKE, None, 4, FAKE, FAKE, ctypes.byref(d), None) == pkv.EINVAL
+    assert L.pkv_append(FAKE, FAKE, FAKE, -1, FAKE, FAKE, ctypes.byref(d), None) == pkv.EINVAL
+    assert L.pkv_append(FAKE, MIS, FAKE, 4, FAKE, FAKE, ctypes.byref(d), None) == pkv.EINVAL
+    assert L.pkv_append(FAKE, FAKE, FAKE, 0, FAKE, FAKE, ctypes.byref(d), None) == pkv.OK
+    bad = _desc(head_dim=80)
+    assert L.pkv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(bad), None) == pkv.EUNSUPPORTED
+
+
+def test_prefill_rejects():
+    def call(**kw):
+        a = dict(q=FAKE, qsl=FAKE, S=2, maxq=16, kc=FAKE, vc=FAKE, bt=FAKE, stride=8, lens=FAKE,
+                 maxL=100, Hq=64, scale=0.1, out=FAKE, odt=pkv.F32, desc=_desc())
+        a.update(kw)
+        return L.pkv_prefill_chunk(a["q"], a["qsl"], a["S"], a["maxq"], a["kc"], a["vc"], a["bt"],
+                                   a["stride"], a["lens"], a["maxL"], a["Hq"], a["scale"], a["out"],
+                                   a["odt"], None, 0, ctypes.byref(a["desc"]), None)
+    assert call(desc=_desc(dtype=pkv.F32)) == pkv.EUNSUPPORTED
+    assert call(q=None) == pkv.EINVAL
+    assert call(qsl=None) == pkv.EINVAL
+    assert call(maxL=10_000) == pkv.EINVAL
+    assert call(Hq=12) == pkv.EINVAL
+    assert call(S=0) == pkv.OK
+
+
+def test_pool_create_rejects_empty():
+    with pytest.raises(pkv.PkvError):
+        pkv.Pool(0)
+
+
+def test_single_hip_runtime_in_process():
+    # libpkv must bind the HIP runtime torch loaded, never a second copy.
+    import subprocess
+    import sys
+    code = ("import re, paged_kv_cache_indirected_amd, torch;"
+            "m=open('/proc/self/maps').read();"
+            "print(len(set(re.findall(r'(\\S*libamdhip64\\S*)', m))))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=ROOT, check=True).stdout.strip()
+    assert out == "1"
