@@ -278,9 +278,9 @@ class Pool:
             raise PkvError(EINVAL, "pkv_pool_create")
 
     def close(self) -> None:
-        if self._h:
+        if self._h and _lib is not None:   # _lib is None during interpreter shutdown
             _lib.pkv_pool_destroy(self._h)
-            self._h = None
+        self._h = None
 
     def __del__(self):
         self.close()
@@ -325,9 +325,9 @@ class Seqs:
             raise PkvError(EINVAL, "pkv_seqs_create")
 
     def close(self) -> None:
-        if self._h:
+        if self._h and _lib is not None:
             _lib.pkv_seqs_destroy(self._h)
-            self._h = None
+        self._h = None
 
     def __del__(self):
         self.close()

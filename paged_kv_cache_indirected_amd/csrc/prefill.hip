@@ -1,13 +1,444 @@
-// Causal chunked prefill on MFMA (placeholder until the kernel lands).
+// Causal chunked prefill over the paged cache on gfx950 (CDNA4) MFMA.
+//
+// What is computed ("LLM Inference: KV Cache, Batching & Scheduling",
+// sections "Chunked prefill" and "The KV cache"): a prompt is processed in
+// fixed-size chunks interleaved with decode; chunking changes the schedule,
+// not the result.  Sequence s holds L_s keys, its chunk of C_s tokens already
+// appended, so chunk token i (0 <= i < C_s) attends keys 0 .. L_s - C_s + i,
+// diagonal included.  Query head h reads KV head h / G.  Keys live in paged
+// blocks (same page, "PagedAttention and vLLM"): key j of sequence s sits in
+// block block_tables[s][j / bs] at offset j % bs.
+//
+// Design (one workgroup = 128 GQA-packed query rows of one (sequence, KV
+// head); row r is chunk token r / G, query head g*G + r % G, so every K/V
+// tile staged once serves all G heads of the group):
+//   * 4 waves x 32 rows.  Keys are processed in tiles of 64.  The workgroup
+//     stages each tile of K ([64][D], row-major) and V (transposed, [D][64],
+//     keys in the MFMA k order) into LDS from the paged cache with 16-byte
+//     loads, double buffered: the next tile's global loads are in flight
+//     while the current tile is computed.
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's
+//     Q rows held in registers for the whole kernel).  Computing the
+//     transpose leaves each lane with 4 consecutive keys of one query column,
+//     which is exactly the B-operand layout P^T needs for the PV product, so
+//     P never leaves registers.
+//   * Online softmax per query column in log2 units: tile max reduced over
+//     the 4 lane groups of the column, lazy running max (rescale only when
+//     the max grows by more than 2^8), masking by select on tiles that cross
+//     the causal diagonal or the end of the context.
+//   * O^T = V^T P^T on MFMA with fp32 accumulation.  P is split into
+//     bf16 hi + lo parts (two MFMAs), so the weights keep ~16 significant
+//     bits instead of bf16's 8; the PV error then stays far below the
+//     2e-3 bar even on rows that attend a handful of keys.
+//   * Grid (Hkv, q-tiles, sequences): the KV head is fastest so all q-tiles
+//     of one (sequence, head) land on one XCD and share its L2; q-tiles run
+//     last-to-first, the longest (most keys) first.
+// Unused slots and keys past the context are staged as zeros and masked; a
+// block id outside the pool is read as zeros without touching memory.
 #include <hip/hip_runtime.h>
 
 #include "pkv_internal.h"
 
 namespace pkv {
+namespace {
 
-int launch_prefill(const PrefillLaunch &)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int NW = 4;                  // waves per workgroup
+constexpr int kThreads = NW * 64;
+constexpr int KT = 64;                 // keys per tile
+constexpr int ROWS = NW * 32;          // query rows per workgroup (32 per wave)
+constexpr float kLazyMax = 8.0f;       // running-max slack, log2 units
+
+template <int D>
+struct PShape {
+    static constexpr int KSTR = D + 8;               // LDS row stride of K (elements)
+    static constexpr int VSTR = KT + 8;              // LDS row stride of V^T (elements)
+    static constexpr int KBUF = KT * KSTR;
+    static constexpr int VBUF = D * VSTR;
+    static constexpr int NDS = D / 32;               // k-steps of S^T over head_dim
+    static constexpr int NDT = D / 16;               // 16-row tiles of O^T
+    static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+    static constexpr int KLD = KT * CPR / kThreads;  // K chunks staged per thread
+    static constexpr int VK = KT * CPR / kThreads;   // V keys staged per thread
+    static_assert(KLD * kThreads == KT * CPR && (VK == 2 || VK == 4), "staging shape");
+};
+
+struct PArgs {
+    const uint16_t *q;
+    const int32_t *qsl;
+    const uint16_t *kc;
+    const uint16_t *vc;
+    const int32_t *tables;
+    const int32_t *lens;
+    void *out;
+    int32_t stride, Hq, Hkv, num_blocks, n_qtiles, out_dtype;
+    float scale_log2;
+};
+
+// LDS column of key kk (0..63) in the transposed V tile: the 8 keys a lane
+// feeds to one PV MFMA, {32s + 4q + i} and {32s + 16 + 4q + i} for i < 4,
+// sit next to each other.
+__device__ __forceinline__ int vpos(int kk)
 {
-    return fail(PKV_EUNSUPPORTED, "pkv_prefill_chunk: not built in this library");
+    return (kk & 32) | ((kk >> 2) & 3) << 3 | ((kk >> 4) & 1) << 2 | (kk & 3);
+}
+
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b)
+{
+    return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b)
+{
+    return (a >> 16) | (b & 0xFFFF0000u);
+}
+__device__ __forceinline__ uint32_t word(const uint4 &v, int i)
+{
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int D, int BS, int G>
+__global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
+{
+    using Sh = PShape<D>;
+    constexpr int TQ = ROWS / G;                     // chunk tokens per workgroup
+    constexpr int NDS = Sh::NDS, NDT = Sh::NDT, CPR = Sh::CPR, VK = Sh::VK;
+    constexpr int KSTR = Sh::KSTR, VSTR = Sh::VSTR;
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][Sh::KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][Sh::VBUF];
+
+    const int g = blockIdx.x;
+    const int qt = a.n_qtiles - 1 - (int)blockIdx.y;
+    const int s = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, quad = lane >> 4;
+
+    const int q0 = a.qsl[s];
+    const int C = a.qsl[s + 1] - q0;
+    int L = a.lens[s];
+    const int cap = a.stride * BS;
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int p0 = L - C;                            // keys before the chunk
+    const int tok0 = qt * TQ;
+    if (tok0 >= C)
+        return;
+    const int tok_end = min(C, tok0 + TQ);
+    const int kend = min(L, p0 + tok_end);           // keys any row of this tile attends
+    const int NT = kend > 0 ? (kend + KT - 1) / KT : 0;
+
+    // This lane's two query columns (one per 16-row MFMA tile).
+    int lim[2];
+    bool valid[2];
+    int64_t qrow[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const int r = w * 32 + ct * 16 + n;
+        const int tok = tok0 + r / G;
+        valid[ct] = tok < tok_end;
+        lim[ct] = valid[ct] ? p0 + tok : -1;
+        qrow[ct] = ((int64_t)(q0 + tok) * a.Hq + g * G + r % G) * D;
+    }
+    // Smallest causal limit over the wave's valid rows (wave-uniform): a
+    // tile entirely at or below it needs no mask.
+    const int wtok = tok0 + (w * 32) / G;
+    const int lim_w = wtok < tok_end ? p0 + wtok : 0x7FFFFFFF;
+
+    bf16x8 qf[2][NDS];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (valid[ct])
+                v = *reinterpret_cast<const uint4 *>(a.q + qrow[ct] + ds * 32 + quad * 8);
+            qf[ct][ds] = __builtin_bit_cast(bf16x8, v);
+        }
+
+    const int32_t *bt = a.tables + (int64_t)s * a.stride;
+    const int64_t hstride = (int64_t)BS * D;         // elements per (block, head) tile
+    const int64_t bstride = (int64_t)a.Hkv * hstride;
+
+    uint4 kst[Sh::KLD], vst[VK];
+    // Global loads of key tile kt into registers.
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < Sh::KLD; ++i) {
+            const int c = tid + kThreads * i;
+            const int kk = c / CPR, cc = c % CPR;
+            const int j = kt * KT + kk;
+            const int id = j < L ? bt[j / BS] : -1;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if ((unsigned)id < (unsigned)a.num_blocks)
+                v = *reinterpret_cast<const uint4 *>(a.kc + id * bstride + g * hstride +
+                                                     (j % BS) * D + cc * 8);
+            kst[i] = v;
+        }
+        const int cc = tid % CPR, k0 = (tid / CPR) * VK;
+#pragma unroll
+        for (int e = 0; e < VK; ++e) {
+            const int j = kt * KT + k0 + e;
+            const int id = j < L ? bt[j / BS] : -1;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if ((unsigned)id < (unsigned)a.num_blocks)
+                v = *reinterpret_cast<const uint4 *>(a.vc + id * bstride + g * hstride +
+                                                     (j % BS) * D + cc * 8);
+            vst[e] = v;
+        }
+    };
+    // Registers -> LDS buffer: K as is, V transposed with its keys placed in
+    // MFMA k order.
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < Sh::KLD; ++i) {
+            const int c = tid + kThreads * i;
+            const int kk = c / CPR, cc = c % CPR;
+            *reinterpret_cast<uint4 *>(&lds_k[buf][kk * KSTR + cc * 8]) = kst[i];
+        }
+        const int cc = tid % CPR, k0 = (tid / CPR) * VK;
+        uint16_t *vt = &lds_v[buf][(cc * 8) * VSTR + vpos(k0)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int wi = e >> 1;
+            if constexpr (VK == 4) {
+                uint2 pr;
+                pr.x = (e & 1) ? hi_pair(word(vst[0], wi), word(vst[1], wi))
+                               : lo_pair(word(vst[0], wi), word(vst[1], wi));
+                pr.y = (e & 1) ? hi_pair(word(vst[2], wi), word(vst[3], wi))
+                               : lo_pair(word(vst[2], wi), word(vst[3], wi));
+                *reinterpret_cast<uint2 *>(vt + e * VSTR) = pr;
+            } else {
+                *reinterpret_cast<uint32_t *>(vt + e * VSTR) =
+                    (e & 1) ? hi_pair(word(vst[0], wi), word(vst[1], wi))
+                            : lo_pair(word(vst[0], wi), word(vst[1], wi));
+            }
+        }
+    };
+
+    f32x4 o[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+            o[dt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+
+    if (NT > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < NT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < NT)
+            load_tile(kt + 1);
+
+        // S^T tile: 64 keys x 32 query columns.
+        f32x4 sacc[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                sacc[ks][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
+                    &lds_k[buf][(ks * 16 + n) * KSTR + ds * 32 + quad * 8]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    sacc[ks][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ct][ds],
+                                                                           sacc[ks][ct], 0, 0, 0);
+            }
+
+        // Online softmax per query column.  Lane holds keys
+        // kt*64 + ks*16 + 4*quad + i of column n.
+        const bool full = kt * KT + KT - 1 <= lim_w;
+        bf16x8 phi[2][2], plo[2][2];
+        bool grew = false;
+        float alpha[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            float x[4][4];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = sacc[ks][ct][i] * a.scale_log2;
+                    if (!full)
+                        v = (kt * KT + ks * 16 + quad * 4 + i <= lim[ct]) ? v : -INFINITY;
+                    x[ks][i] = v;
+                    mt = fmaxf(mt, v);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const bool up = mt > m[ct] + kLazyMax;
+            const float mn = up ? mt : m[ct];
+            alpha[ct] = up ? __builtin_amdgcn_exp2f(m[ct] - mn) : 1.0f;
+            grew |= up;
+            m[ct] = mn;
+            const bool dead = (mn == -INFINITY);
+            float sum = 0.0f;
+            float pv[4][4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pv[ks][i] = dead ? 0.0f : __builtin_amdgcn_exp2f(x[ks][i] - mn);
+                    sum += pv[ks][i];
+                }
+            lsum[ct] = __builtin_fmaf(lsum[ct], alpha[ct], sum);
+            // P^T operands for the two 32-key k-steps: keys {32s + 4q + i}
+            // then {32s + 16 + 4q + i}; hi part and the rounding remainder.
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                bf16x8 h, lo;
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const float p0v = pv[2 * s2 + half][i], p1v = pv[2 * s2 + half][i + 1];
+                        const bf16x2_t hp = __builtin_convertvector(f32x2{p0v, p1v}, bf16x2_t);
+                        const float r0 = p0v - (float)hp[0], r1 = p1v - (float)hp[1];
+                        const bf16x2_t lp = __builtin_convertvector(f32x2{r0, r1}, bf16x2_t);
+                        h[half * 4 + i] = hp[0];
+                        h[half * 4 + i + 1] = hp[1];
+                        lo[half * 4 + i] = lp[0];
+                        lo[half * 4 + i + 1] = lp[1];
+                    }
+                phi[ct][s2] = h;
+                plo[ct][s2] = lo;
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    o[dt][ct] *= alpha[ct];
+        }
+
+        // O^T += V^T P^T (hi and lo parts).
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
+                    &lds_v[buf][(dt * 16 + n) * VSTR + 32 * s2 + 8 * quad]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct][s2], o[dt][ct],
+                                                                        0, 0, 0);
+                    o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[ct][s2], o[dt][ct],
+                                                                        0, 0, 0);
+                }
+            }
+
+        if (kt + 1 < NT)
+            store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Normalise and write: lane holds O^T[dt*16 + 4*quad + i][column n].
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        float l = lsum[ct];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (!valid[ct])
+            continue;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int64_t idx = qrow[ct] + dt * 16 + quad * 4;
+            const f32x4 r = o[dt][ct] * inv;
+            if (a.out_dtype == PKV_F32) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + idx) = r;
+            } else {
+                uint2 pk;
+                pk.x = (uint32_t)bf16_rne(r[0]) | ((uint32_t)bf16_rne(r[1]) << 16);
+                pk.y = (uint32_t)bf16_rne(r[2]) | ((uint32_t)bf16_rne(r[3]) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + idx) = pk;
+            }
+        }
+    }
+}
+
+using KernelFn = void (*)(PArgs);
+
+template <int D, int BS>
+KernelFn pick_g(int G)
+{
+    switch (G) {
+    case 1: return k_prefill<D, BS, 1>;
+    case 2: return k_prefill<D, BS, 2>;
+    case 4: return k_prefill<D, BS, 4>;
+    case 8: return k_prefill<D, BS, 8>;
+    default: return nullptr;
+    }
+}
+
+KernelFn pick(int D, int BS, int G)
+{
+    if (D == 64)
+        return BS == 16 ? pick_g<64, 16>(G) : pick_g<64, 32>(G);
+    return BS == 16 ? pick_g<128, 16>(G) : pick_g<128, 32>(G);
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillLaunch &p)
+{
+    if (p.num_seqs == 0 || p.max_query_len == 0)
+        return PKV_OK;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    KernelFn fn = pick(p.head_dim, p.block_size, G);
+    if (!fn)
+        return fail(PKV_EUNSUPPORTED, "pkv_prefill_chunk: no kernel for head_dim %d, block %d, "
+                    "group %d", p.head_dim, p.block_size, G);
+    const int tq = ROWS / G;
+    const int64_t nqt = ((int64_t)p.max_query_len + tq - 1) / tq;
+    if (nqt > 65535)
+        return fail(PKV_EINVAL, "pkv_prefill_chunk: max_query_len %d needs %lld q-tiles",
+                    p.max_query_len, (long long)nqt);
+    PArgs a;
+    a.q = static_cast<const uint16_t *>(p.q);
+    a.qsl = p.query_start;
+    a.kc = static_cast<const uint16_t *>(p.k_cache);
+    a.vc = static_cast<const uint16_t *>(p.v_cache);
+    a.tables = p.block_tables;
+    a.lens = p.context_lens;
+    a.out = p.out;
+    a.stride = p.table_stride;
+    a.Hq = p.num_q_heads;
+    a.Hkv = p.num_kv_heads;
+    a.num_blocks = p.num_blocks;
+    a.n_qtiles = (int32_t)nqt;
+    a.out_dtype = p.out_dtype;
+    a.scale_log2 = p.scale * 1.4426950408889634f;
+    hipStream_t st = reinterpret_cast<hipStream_t>(p.stream);
+    hipLaunchKernelGGL(fn, dim3(p.num_kv_heads, (unsigned)nqt, p.num_seqs), dim3(kThreads), 0, st,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(PKV_EHIP, "pkv_prefill_chunk: launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
 }
 
 }  // namespace pkv

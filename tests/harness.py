@@ -82,3 +82,37 @@ def max_err(out: torch.Tensor, ref: np.ndarray, pairs=None) -> float:
     for b, h in pairs:
         e = max(e, float(np.max(np.abs(o[b, h] - ref[b, h]))))
     return e
+
+
+def prefill_state(batch: synth.PrefillBatch, pool_seed=None, poison=None):
+    """Append every sequence's prior rows and its chunk through the pool and
+    pkv_append (the chunk is in the cache before the prefill call).  Returns
+    (cache, q, query_start, tables, lens, max_len)."""
+    sh = batch.shape
+    seed = batch.pool_seed if pool_seed is None else pool_seed
+    cache = PagedCache(batch.pool_blocks, sh.Hkv, sh.block_size, sh.D, DT[sh.dtype],
+                       pool_seed=seed, poison=poison)
+    ids = list(range(len(batch.chunk)))
+    cache.add_sequences(ids, batch.lens, batch.k, batch.v)
+    tables, lens, max_len = cache.tables(ids)
+    q = to_device_rows(batch.q, DT[sh.dtype], cache.device)
+    qs = torch.from_numpy(batch.query_start.astype(np.int32)).to(cache.device)
+    return cache, q, qs, tables, lens, max_len
+
+
+def run_prefill(cache: PagedCache, q, qs, tables, lens, max_len, scale, max_query_len,
+                out_dtype=torch.float32):
+    out = torch.empty(tuple(q.shape), dtype=out_dtype, device=q.device)
+    pkv.prefill_chunk(q, qs, cache.k_cache, cache.v_cache, tables, lens, scale, out, cache.desc,
+                      max_query_len, max_len)
+    torch.cuda.synchronize()
+    return out
+
+
+def sample_rows(T, Hq, n, seed):
+    """n distinct (token row, head) pairs, or None for all when T*Hq <= n."""
+    g = np.random.default_rng(seed)
+    if T * Hq <= n:
+        return None
+    flat = g.choice(T * Hq, size=n, replace=False)
+    return np.stack([flat // Hq, flat % Hq], axis=1).astype(np.int32)

@@ -1,0 +1,129 @@
+"""Causal chunked prefill on the MFMA path against the fp64 oracle ("LLM
+Inference: KV Cache, Batching & Scheduling", section "Chunked prefill": a
+chunk of the prompt attends every earlier key and itself, and splitting the
+prompt into chunks does not change the result).
+
+Bar: max abs error 2e-3 for bf16 inputs on fp32 output; bitwise equality for
+the placement and poison invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from harness import (TOL, decode_state, max_err, prefill_state, run_decode, run_prefill,
+                     sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(batch, rows=None, label=""):
+    C = int(batch.chunk.max())
+    say(f"[prefill] {label} S={len(batch.chunk)} prior={batch.prior.tolist()} "
+        f"chunk={batch.chunk.tolist()} G={batch.shape.Hq // batch.shape.Hkv} "
+        f"D={batch.shape.D} bs={batch.shape.block_size}")
+    st = prefill_state(batch)
+    out = run_prefill(*st, batch.shape.scale, C)
+    ref = oracle.prefill(batch.q, batch.query_start, batch.k, batch.v, batch.lens,
+                         batch.shape.scale, rows=rows)
+    o = out.float().cpu().numpy().astype(np.float64)
+    if rows is None:
+        err = float(np.max(np.abs(o - ref))) if o.size else 0.0
+    else:
+        err = max(float(np.max(np.abs(o[t, h] - ref[t, h]))) for t, h in rows)
+    say(f"  max abs err {err:.3e}")
+    assert np.isfinite(err) and err <= TOL["bf16"], err
+    return out
+
+
+def test_cfg5_prefill_sampled():
+    pre, _ = synth.cfg5()
+    T = int(pre.chunk.sum())
+    _check(pre, rows=sample_rows(T, pre.shape.Hq, 1024, 51), label="cfg5")
+
+
+def test_cfg5_prefill_first_and_last_rows_full():
+    # Every head of the first and last token of each chunk: the shortest and
+    # the longest rows, the diagonal tile included.
+    pre, _ = synth.cfg5()
+    qs = pre.query_start
+    rows = [(int(t), h) for b in range(len(pre.chunk))
+            for t in (qs[b], qs[b] + 1, qs[b + 1] - 1) for h in range(pre.shape.Hq)]
+    _check(pre, rows=np.array(rows, dtype=np.int32), label="cfg5-edges")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_shape_sweep_ragged(D, bs, G):
+    # Priors at 0, inside a block, on a block boundary; chunks of 1, ragged
+    # against the 128-row tile and the 64-key tile.
+    b = synth.custom_prefill(300 + G + D + bs, prior=[0, 5, 64, 200], chunk=[37, 1, 130, 77],
+                             Hq=2 * G, Hkv=2, D=D, block_size=bs)
+    _check(b, label="sweep")
+
+
+def test_first_chunk_of_a_prompt_p0_zero():
+    b = synth.custom_prefill(310, prior=[0, 0], chunk=[512, 3], Hq=64, Hkv=8, D=128,
+                             block_size=16)
+    _check(b, label="p0=0")
+
+
+def test_prefill_row_equals_decode_at_that_length():
+    b = synth.custom_prefill(311, prior=[100], chunk=[40], Hq=16, Hkv=2, D=128, block_size=16)
+    st = prefill_state(b)
+    out = run_prefill(*st, b.shape.scale, 40).cpu().numpy()
+    for i in (0, 17, 39):
+        L = 100 + i + 1
+        dec = synth.DecodeBatch(0, "row", b.shape, np.array([L]), b.q[i:i + 1], b.k[:L], b.v[:L],
+                                pool_blocks=64, pool_seed=5)
+        o_dec = run_decode(*decode_state(dec), b.shape.scale).cpu().numpy()
+        assert np.max(np.abs(out[i] - o_dec[0])) <= 2 * TOL["bf16"]
+
+
+def test_chunk_split_independence():
+    # One 256-token chunk vs the same prompt prefilled as 4 chunks of 64.
+    whole = synth.custom_prefill(312, prior=[300], chunk=[256], Hq=16, Hkv=2, D=128,
+                                 block_size=16)
+    o_whole = run_prefill(*prefill_state(whole), whole.shape.scale, 256).cpu().numpy()
+    parts = []
+    for c in range(4):
+        P = 300 + 64 * c
+        L = P + 64
+        pb = synth.PrefillBatch(whole.shape, np.array([P]), np.array([64]),
+                                whole.q[64 * c:64 * (c + 1)], whole.k[:L], whole.v[:L],
+                                pool_blocks=64, pool_seed=9 + c)
+        parts.append(run_prefill(*prefill_state(pb), whole.shape.scale, 64).cpu().numpy())
+    o_parts = np.concatenate(parts)
+    assert np.max(np.abs(o_whole - o_parts)) <= 2 * TOL["bf16"]
+    ref = oracle.prefill(whole.q, whole.query_start, whole.k, whole.v, whole.lens,
+                         whole.shape.scale)
+    assert np.max(np.abs(o_parts - ref)) <= TOL["bf16"]
+
+
+def test_placement_and_poison_bitwise():
+    b = synth.custom_prefill(313, prior=[33, 0], chunk=[70, 20], Hq=16, Hkv=2, D=128,
+                             block_size=16)
+    outs = [run_prefill(*prefill_state(b, pool_seed=s, poison=p), b.shape.scale, 70)
+            for s, p in ((None, None), (0, None), (77, 0x0000), (5, 0x7F7F))]
+    assert torch.isfinite(outs[0]).all()
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o)
+
+
+def test_bf16_output():
+    b = synth.custom_prefill(314, prior=[128], chunk=[64], Hq=64, Hkv=8, D=128, block_size=16)
+    out = run_prefill(*prefill_state(b), b.shape.scale, 64, out_dtype=torch.bfloat16)
+    ref = oracle.prefill(b.q, b.query_start, b.k, b.v, b.lens, b.shape.scale)
+    o = out.float().cpu().numpy().astype(np.float64)
+    half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8)
+    assert np.all(np.abs(o - ref) <= 2e-3 + half_ulp)
+
+
+def test_repeat_is_bitwise_deterministic():
+    b = synth.custom_prefill(315, prior=[500], chunk=[128], Hq=64, Hkv=8, D=128, block_size=16)
+    st = prefill_state(b)
+    o1 = run_prefill(*st, b.shape.scale, 128)
+    o2 = run_prefill(*st, b.shape.scale, 128)
+    assert torch.equal(o1, o2)
