@@ -94,7 +94,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
-    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0, help="workgroups per KV head (0: library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -117,17 +117,16 @@ def main():
     out = torch.empty((batch.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
     desc = states[0]["cache"].desc
     max_len = max(s["max_len"] for s in states)
-    pt = args.partition_tokens
-    nbytes = pkv.decode_workspace_bytes(batch.B, sh.Hq, max_len, desc, pt)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-    part_tokens = pt or pkv.decode_partition_tokens(batch.B, sh.Hq, max_len, desc)
+    nbytes = pkv.decode_workspace_bytes(batch.B, sh.Hq, max_len, desc, args.splits)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    splits = args.splits or pkv.decode_num_splits(batch.B, sh.Hq, max_len, desc)
 
     def step(i):
         s = states[i % len(states)]
         c = s["cache"]
         pkv.append(s["k_new"], s["v_new"], s["slots"], c.k_cache, c.v_cache, c.desc)
         pkv.decode(q, c.k_cache, c.v_cache, s["tables"], s["lens"], sh.scale, out, c.desc,
-                   max_len, workspace=ws, partition_tokens=pt)
+                   max_len, workspace=ws, num_splits=args.splits)
 
     for i in range(args.warmup):
         step(i)
@@ -150,7 +149,7 @@ def main():
         c = s["cache"]
         evs[i][0].record()
         pkv.decode(q, c.k_cache, c.v_cache, s["tables"], s["lens"], sh.scale, out, c.desc,
-                   max_len, workspace=ws, partition_tokens=pt)
+                   max_len, workspace=ws, num_splits=args.splits)
         evs[i][1].record()
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
@@ -178,13 +177,13 @@ def main():
             "global_batch": batch.B,
             "context_tokens": int(batch.lens.sum()),
             "pool_copies_rotated": len(states),
-            "partition_tokens": part_tokens,
+            "splits_per_kv_head": splits,
         },
         "pct_of_hbm_peak": round(100.0 * gbs_step / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(batch.B / (ms_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pkv_decode (partition pass + LSE merge)",
+            "kernel": "pkv_decode (balanced split pass + LSE merge)",
             "achieved": round(gbs_dec, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -69,7 +69,7 @@ const char *pkv_strerror(int code);
 const char *pkv_last_error(void);
 /* ABI version of this header (bumped on incompatible change). */
 int pkv_abi_version(void);
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* ------------------------------------------------------------------------
  * KV append ([KV-prep] "The KV cache": the new token's K and V are appended
@@ -101,28 +101,35 @@ int pkv_append(const void *k, const void *v, const int32_t *slot_mapping, int32_
  *   block_tables  [num_seqs][block_table_stride] int32; entries past
  *                 ceil(L / block_size) are not read
  *   context_lens  [num_seqs] int32
- *   max_context_len  host-side upper bound of context_lens (sizes the grid;
- *                 a sequence longer than it is a precondition violation)
+ *   max_context_len  host-side upper bound of context_lens (sizes the split;
+ *                 a longer device length is clamped to it)
  *   out           [num_seqs][num_q_heads][head_dim]; out_dtype PKV_F32 or
  *                 PKV_BF16 (round to nearest even)
- *   partition_tokens  context tokens per split partition; 0 = library choice
- *                 (pkv_decode_partition_tokens); otherwise a positive
- *                 multiple of 4 * block_size
+ *   num_splits    workgroups per KV head; 0 = library choice
+ *                 (pkv_decode_num_splits).  The blocks of all sequences are
+ *                 laid end to end and cut into num_splits equal ranges, so
+ *                 every workgroup reads the same number of K/V bytes; a
+ *                 sequence cut between ranges is finished by a log-sum-exp
+ *                 merge pass (a second, small launch).  The result depends on num_splits only through
+ *                 fp32 rounding, and is bitwise reproducible for a given
+ *                 (context_lens, num_splits).
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...)
- *                 bytes for the split partials (fp32); may be NULL when that
- *                 size is 0.  Its contents need no initialisation.
- * Supported: dtype F32/BF16, head_dim 64/128, block_size 16/32,
+ *                 bytes (never NULL for num_seqs > 0); its contents need no
+ *                 initialisation and are overwritten.  Calls that share a
+ *                 workspace must not run concurrently.
+ * Sequences are processed in launches of at most 1024; num_seqs may be
+ * larger.  Supported: dtype F32/BF16, head_dim 64/128, block_size 16/32,
  * G in {1, 2, 4, 8}.
  */
-int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
-                                    int32_t max_context_len, const pkv_cache_desc *c);
+int32_t pkv_decode_num_splits(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                              const pkv_cache_desc *c);
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                                  int32_t partition_tokens, const pkv_cache_desc *c);
+                                  int32_t num_splits, const pkv_cache_desc *c);
 int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
                const int32_t *block_tables, int32_t block_table_stride,
                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
                int32_t max_context_len, float scale, void *out, int32_t out_dtype,
-               int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+               int32_t num_splits, void *workspace, size_t workspace_bytes,
                const pkv_cache_desc *c, void *stream);
 
 /* ------------------------------------------------------------------------

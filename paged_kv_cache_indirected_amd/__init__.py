@@ -64,7 +64,7 @@ _sig("pkv_strerror", ctypes.c_char_p, ctypes.c_int)
 _sig("pkv_last_error", ctypes.c_char_p)
 _sig("pkv_abi_version", ctypes.c_int)
 _sig("pkv_append", ctypes.c_int, _P, _P, _P, _i32, _P, _P, _DESC, _P)
-_sig("pkv_decode_partition_tokens", _i32, _i32, _i32, _i32, _DESC)
+_sig("pkv_decode_num_splits", _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, ctypes.c_float, _P,
      _i32, _i32, _P, _sz, _DESC, _P)
@@ -193,23 +193,24 @@ def append(k, v, slot_mapping, k_cache, v_cache, desc: CacheDesc, stream=None) -
     _check(rc, "pkv_append")
 
 
-def decode_partition_tokens(num_seqs: int, num_q_heads: int, max_context_len: int,
-                            desc: CacheDesc) -> int:
-    return int(_lib.pkv_decode_partition_tokens(num_seqs, num_q_heads, max_context_len,
-                                                ctypes.byref(desc.c())))
+def decode_num_splits(num_seqs: int, num_q_heads: int, max_context_len: int,
+                      desc: CacheDesc) -> int:
+    """pkv_decode_num_splits: the library's workgroups per KV head."""
+    return int(_lib.pkv_decode_num_splits(num_seqs, num_q_heads, max_context_len,
+                                          ctypes.byref(desc.c())))
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
-                           desc: CacheDesc, partition_tokens: int = 0) -> int:
+                           desc: CacheDesc, num_splits: int = 0) -> int:
     return int(_lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
-                                               partition_tokens, ctypes.byref(desc.c())))
+                                               num_splits, ctypes.byref(desc.c())))
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, desc: CacheDesc,
-           max_context_len: int, workspace=None, partition_tokens: int = 0, stream=None) -> None:
+           max_context_len: int, workspace=None, num_splits: int = 0, stream=None) -> None:
     """pkv_decode: out[b][h] = softmax(scale q[b][h] K^T) V over the paged
     context of sequence b.  ``workspace`` is a uint8 GPU tensor of at least
-    ``decode_workspace_bytes(...)`` bytes (None when that is 0)."""
+    ``decode_workspace_bytes(...)`` bytes."""
     torch = _torch()
     B, Hq, D = q.shape
     _need(D == desc.head_dim and _dtype_code(q) == desc.dtype, "q must be [B][Hq][head_dim]")
@@ -224,7 +225,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, d
                          int(block_tables.shape[1]) if block_tables.dim() == 2 else 0,
                          _dev(context_lens, "context_lens", torch.int32), B, Hq,
                          int(max_context_len), float(scale), _dev(out, "out"), _dtype_code(out),
-                         int(partition_tokens), _dev(workspace, "workspace"), ws_bytes,
+                         int(num_splits), _dev(workspace, "workspace"), ws_bytes,
                          ctypes.byref(desc.c()), _stream(stream))
     _check(rc, "pkv_decode")
 

@@ -18,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")   # measurement probes, loaded by the benchmark only
 OBJ = os.path.join(ROOT, "_build", "pkv")
 
 HOST_SRC = ["errors.cpp", "pool.cpp", "api.cpp"]
@@ -63,6 +64,9 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(OBJ, s + ".o") for s in HOST_SRC + HIP_SRC]
     _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, *HIP_FLAGS, "-shared", os.path.join(CSRC, "probe.hip"), "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

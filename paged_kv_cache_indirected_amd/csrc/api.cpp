@@ -9,8 +9,6 @@ using pkv::fail;
 
 namespace {
 
-constexpr int kWavesPerGroup = 4;   // decode workgroup: 4 waves, each takes every 4th block
-
 int check_desc(const pkv_cache_desc *c, const char *who)
 {
     if (!c)
@@ -51,35 +49,47 @@ int check_heads(int32_t hq, const pkv_cache_desc *c, const char *who)
     return PKV_OK;
 }
 
-// Partition size: the largest power-of-two multiple of 4 blocks, at most 2048
-// tokens, that still gives at least 2048 workgroups (8 per CU on 256 CUs) for
-// the (sequence, KV head) pairs at the longest context.
-int32_t auto_partition_tokens(int32_t num_seqs, int32_t max_ctx, const pkv_cache_desc *c)
+// Decode split: W workgroups per KV head cut the batch's blocks into equal
+// ranges.  W fills the chip with kGroupsPerCU resident workgroups per CU, but
+// is never larger than gives each of a workgroup's 4 waves 2 blocks of the
+// batch's upper-bound block count.
+constexpr int kGroupsPerCU = 2;
+
+int64_t blocks_bound(int32_t num_seqs, int32_t max_ctx, const pkv_cache_desc *c)
 {
-    const int32_t unit = kWavesPerGroup * c->block_size;
-    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * c->num_kv_heads;
-    const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
-    int32_t pt = 2048;
-    while (pt > unit && pairs * ((ctx + pt - 1) / pt) < 2048)
-        pt /= 2;
-    return pt < unit ? unit : pt;
+    const int64_t bc = num_seqs < pkv::kDecodeMaxSeqs ? num_seqs : pkv::kDecodeMaxSeqs;
+    const int64_t ctx = max_ctx > 0 ? max_ctx : 0;
+    return bc * ((ctx + c->block_size - 1) / c->block_size);
 }
 
-int32_t max_partitions(int32_t max_ctx, int32_t pt)
+int32_t auto_splits(int32_t num_seqs, int32_t max_ctx, const pkv_cache_desc *c)
 {
-    const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
-    return (int32_t)((ctx + pt - 1) / pt);
+    const int64_t cap = ((int64_t)pkv::device_cu_count() * kGroupsPerCU + c->num_kv_heads - 1) /
+                        c->num_kv_heads;
+    const int64_t want = (blocks_bound(num_seqs, max_ctx, c) + 7) / 8;
+    int64_t w = want < cap ? want : cap;
+    w = w < 1 ? 1 : (w > 65535 ? 65535 : w);
+    return (int32_t)w;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Bytes of the split partials: o [B][Hq][P][D] then (m, l) [B][Hq][P][2], fp32.
-size_t ws_bytes(int32_t B, int32_t hq, int32_t P, int32_t D)
+// Workspace: block prefix sums [Bc + 1] int32, then partial outputs
+// [W + Bc][Hq][D] and (m, l) [W + Bc][Hq][2] fp32, Bc = min(B, kDecodeMaxSeqs).
+struct WsLayout {
+    size_t pref, o, ml, total;
+};
+
+WsLayout ws_layout(int32_t B, int32_t hq, int32_t W, int32_t D)
 {
-    if (P <= 1 || B <= 0)
-        return 0;
-    const size_t rows = (size_t)B * hq * P;
-    return align256(rows * D * sizeof(float)) + rows * 2 * sizeof(float);
+    const size_t bc = (size_t)(B < pkv::kDecodeMaxSeqs ? B : pkv::kDecodeMaxSeqs);
+    const size_t pieces = (size_t)W + bc;
+    WsLayout l;
+    l.pref = 0;
+    l.o = align256((bc + 1) * sizeof(int32_t));
+    l.ml = l.o + align256(pieces * hq * D * sizeof(float));
+    l.total = l.ml + pieces * hq * 2 * sizeof(float);
+    return l;
 }
 
 }  // namespace
@@ -107,31 +117,31 @@ extern "C" int pkv_append(const void *k, const void *v, const int32_t *slot_mapp
     return pkv::launch_append(a);
 }
 
-extern "C" int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads,
-                                               int32_t max_context_len, const pkv_cache_desc *c)
+extern "C" int32_t pkv_decode_num_splits(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t max_context_len, const pkv_cache_desc *c)
 {
     (void)num_q_heads;
-    if (check_desc(c, "pkv_decode_partition_tokens"))
+    if (check_desc(c, "pkv_decode_num_splits") || num_seqs < 0)
         return 0;
-    return auto_partition_tokens(num_seqs, max_context_len, c);
+    return auto_splits(num_seqs, max_context_len, c);
 }
 
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                             int32_t max_context_len, int32_t partition_tokens,
+                                             int32_t max_context_len, int32_t num_splits,
                                              const pkv_cache_desc *c)
 {
-    if (check_desc(c, "pkv_decode_workspace_bytes") || num_seqs < 0 || num_q_heads <= 0)
+    if (check_desc(c, "pkv_decode_workspace_bytes") || num_seqs <= 0 || num_q_heads <= 0 ||
+        num_splits < 0)
         return 0;
-    const int32_t pt = partition_tokens > 0 ? partition_tokens
-                                            : auto_partition_tokens(num_seqs, max_context_len, c);
-    return ws_bytes(num_seqs, num_q_heads, max_partitions(max_context_len, pt), c->head_dim);
+    const int32_t W = num_splits > 0 ? num_splits : auto_splits(num_seqs, max_context_len, c);
+    return ws_layout(num_seqs, num_q_heads, W, c->head_dim).total;
 }
 
 extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
                           const int32_t *block_tables, int32_t block_table_stride,
                           const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
                           int32_t max_context_len, float scale, void *out, int32_t out_dtype,
-                          int32_t partition_tokens, void *workspace, size_t workspace_bytes,
+                          int32_t num_splits, void *workspace, size_t workspace_bytes,
                           const pkv_cache_desc *c, void *stream)
 {
     static const char *who = "pkv_decode";
@@ -139,8 +149,8 @@ extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cach
     int rc = check_desc(c, who);
     if (rc || (rc = check_heads(num_q_heads, c, who)))
         return rc;
-    if (num_seqs < 0 || num_seqs > 65535)
-        return fail(PKV_EINVAL, "%s: num_seqs %d (0 .. 65535)", who, num_seqs);
+    if (num_seqs < 0)
+        return fail(PKV_EINVAL, "%s: num_seqs %d", who, num_seqs);
     if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
         return fail(PKV_EINVAL, "%s: out_dtype %d", who, out_dtype);
     if (!std::isfinite(scale))
@@ -152,28 +162,23 @@ extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cach
         return fail(PKV_EINVAL,
                     "%s: max_context_len %d must lie in [0, block_table_stride %d * block_size]",
                     who, max_context_len, block_table_stride);
-    const int32_t unit = kWavesPerGroup * c->block_size;
-    if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % unit != 0))
-        return fail(PKV_EINVAL, "%s: partition_tokens %d must be 0 or a multiple of %d", who,
-                    partition_tokens, unit);
+    if (blocks_bound(num_seqs, max_context_len, c) > INT32_MAX)
+        return fail(PKV_EINVAL, "%s: %d sequences of up to %d tokens exceed 2^31 blocks per launch",
+                    who, num_seqs, max_context_len);
+    if (num_splits < 0 || num_splits > 65535)
+        return fail(PKV_EINVAL, "%s: num_splits %d (0 .. 65535)", who, num_splits);
     if ((rc = check_ptr(q, "q", who)) || (rc = check_ptr(k_cache, "k_cache", who)) ||
         (rc = check_ptr(v_cache, "v_cache", who)) || (rc = check_ptr(out, "out", who)))
         return rc;
     if (!block_tables || !context_lens)
         return fail(PKV_EINVAL, "%s: block_tables or context_lens is NULL", who);
-    const int32_t pt = partition_tokens > 0 ? partition_tokens
-                                            : auto_partition_tokens(num_seqs, max_context_len, c);
-    const int32_t P = max_partitions(max_context_len, pt);
-    if (P > 65535)
-        return fail(PKV_EINVAL, "%s: %d partitions exceed the grid", who, P);
-    const size_t need = ws_bytes(num_seqs, num_q_heads, P, c->head_dim);
-    if (need > 0) {
-        if ((rc = check_ptr(workspace, "workspace", who)))
-            return rc;
-        if (workspace_bytes < need)
-            return fail(PKV_EINVAL, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
-                        need);
-    }
+    const int32_t W = num_splits > 0 ? num_splits : auto_splits(num_seqs, max_context_len, c);
+    const WsLayout lay = ws_layout(num_seqs, num_q_heads, W, c->head_dim);
+    if ((rc = check_ptr(workspace, "workspace", who)))
+        return rc;
+    if (workspace_bytes < lay.total)
+        return fail(PKV_EINVAL, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                    lay.total);
     pkv::DecodeLaunch d{};
     d.q = q;
     d.k_cache = k_cache;
@@ -188,17 +193,15 @@ extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cach
     d.block_size = c->block_size;
     d.head_dim = c->head_dim;
     d.dtype = c->dtype;
-    d.partition_blocks = pt / c->block_size;
-    d.max_partitions = P;
+    d.max_context_len = max_context_len;
+    d.num_splits = W;
     d.scale = scale;
     d.out = out;
     d.out_dtype = out_dtype;
-    if (need > 0) {
-        const size_t rows = (size_t)num_seqs * num_q_heads * P;
-        d.ws_o = static_cast<float *>(workspace);
-        d.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                            align256(rows * c->head_dim * sizeof(float)));
-    }
+    char *ws = static_cast<char *>(workspace);
+    d.ws_pref = reinterpret_cast<int32_t *>(ws + lay.pref);
+    d.ws_o = reinterpret_cast<float *>(ws + lay.o);
+    d.ws_ml = reinterpret_cast<float *>(ws + lay.ml);
     d.stream = stream;
     return pkv::launch_decode(d);
 }

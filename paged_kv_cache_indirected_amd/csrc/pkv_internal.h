@@ -14,6 +14,10 @@ void clear_error();
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Sequences per decode launch: the kernel keeps the batch's block prefix
+// sums in LDS; larger batches go in several launches.
+constexpr int32_t kDecodeMaxSeqs = 1024;
+
 // Launch arguments of the decode kernels, already validated by the C ABI.
 struct DecodeLaunch {
     const void *q;
@@ -29,16 +33,19 @@ struct DecodeLaunch {
     int32_t block_size;
     int32_t head_dim;
     int32_t dtype;
-    int32_t partition_blocks;  // blocks of context per workgroup
-    int32_t max_partitions;    // grid extent over partitions
+    int32_t max_context_len;   // device lengths are clamped to this
+    int32_t num_splits;        // workgroups per KV head
     float scale;
     void *out;
     int32_t out_dtype;
-    float *ws_o;               // [B][Hq][max_partitions][D] un-normalised partial outputs
-    float *ws_ml;              // [B][Hq][max_partitions][2] running max (log2 units) and sum
+    int32_t *ws_pref;          // [Bc + 1] block prefix sums
+    float *ws_o;               // [Hkv][W + Bc][G][D] partial outputs
+    float *ws_ml;              // [Hkv][W + Bc][G][2] running max (log2 units) and sum
     void *stream;
 };
 int launch_decode(const DecodeLaunch &a);
+// Compute units of the current device (256 if it cannot be queried).
+int32_t device_cu_count();
 
 struct AppendLaunch {
     const void *k;

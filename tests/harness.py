@@ -55,13 +55,13 @@ def decode_state(batch: synth.DecodeBatch, pool_seed=None, poison=None, share_pr
 
 
 def run_decode(cache: PagedCache, q, tables, lens, max_len, scale, out_dtype=torch.float32,
-               partition_tokens=0):
+               num_splits=0):
     B, Hq, D = q.shape
     out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
-    nbytes = pkv.decode_workspace_bytes(B, Hq, max_len, cache.desc, partition_tokens)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
+    nbytes = pkv.decode_workspace_bytes(B, Hq, max_len, cache.desc, num_splits)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     pkv.decode(q, cache.k_cache, cache.v_cache, tables, lens, scale, out, cache.desc, max_len,
-               workspace=ws, partition_tokens=partition_tokens)
+               workspace=ws, num_splits=num_splits)
     torch.cuda.synchronize()
     return out
 

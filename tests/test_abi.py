@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_strerror():
-    assert pkv.abi_version() == 1
+    assert pkv.abi_version() == 2
     for code in (pkv.OK, pkv.EINVAL, pkv.EUNSUPPORTED, pkv.ENOBLOCKS, pkv.ESTATE, pkv.EHIP):
         assert pkv.strerror(code) and pkv.strerror(code) != "unknown error code"
 
@@ -63,12 +63,13 @@ def _decode(**kw):
     (dict(desc=_desc(dtype=7)), pkv.EUNSUPPORTED),
     (dict(desc=_desc(num_blocks=0)), pkv.EINVAL),
     (dict(maxL=16 * 8 + 1), pkv.EINVAL),       # beyond stride * block_size
-    (dict(pt=48), pkv.EINVAL),                 # not a multiple of 4 blocks
+    (dict(pt=-1), pkv.EINVAL),                 # negative split count
+    (dict(pt=70000), pkv.EINVAL),              # split count beyond the grid
     (dict(odt=3), pkv.EINVAL),
     (dict(scale=float("nan")), pkv.EINVAL),
     (dict(B=-1), pkv.EINVAL),
-    (dict(maxL=128, pt=64, wsb=16), pkv.EINVAL),   # short workspace
-    (dict(maxL=128, pt=64, ws=None), pkv.EINVAL),
+    (dict(maxL=128, pt=4, wsb=16), pkv.EINVAL),    # short workspace
+    (dict(maxL=128, pt=0, ws=None), pkv.EINVAL),   # the workspace is always needed
 ])
 def test_decode_rejects(kw, code):
     assert _decode(**kw) == code
@@ -81,14 +82,21 @@ def test_decode_empty_batch_is_a_noop():
 
 def test_workspace_size_rules():
     d = _desc()
-    # One partition per sequence needs no workspace.
-    assert L.pkv_decode_workspace_bytes(4, 64, 256, 256, ctypes.byref(d)) == 0
-    n = L.pkv_decode_workspace_bytes(4, 64, 1000, 256, ctypes.byref(d))
-    P = (1000 + 255) // 256
-    rows = 4 * 64 * P
-    assert n >= rows * 128 * 4 + rows * 2 * 4
-    pt = L.pkv_decode_partition_tokens(32, 64, 4096, ctypes.byref(d))
-    assert pt > 0 and pt % (4 * 16) == 0
+    # Prefix sums [B + 1] plus (W + B) partial rows of every query head.
+    for B, W in ((4, 1), (4, 37), (32, 128), (3000, 128)):
+        n = L.pkv_decode_workspace_bytes(B, 64, 1000, W, ctypes.byref(d))
+        bc = min(B, 1024)
+        pieces = W + bc
+        assert n >= (bc + 1) * 4 + pieces * 64 * 128 * 4 + pieces * 64 * 2 * 4
+    assert L.pkv_decode_workspace_bytes(0, 64, 1000, 8, ctypes.byref(d)) == 0
+    assert L.pkv_decode_workspace_bytes(4, 64, 1000, -1, ctypes.byref(d)) == 0
+    # Library choice: at least 1, at most 65535, and no more than gives each
+    # of a workgroup's 4 waves 2 blocks of the batch's upper-bound block count.
+    assert L.pkv_decode_num_splits(1, 64, 16, ctypes.byref(d)) == 1
+    w = L.pkv_decode_num_splits(32, 64, 4096, ctypes.byref(d))
+    assert 1 <= w <= 32 * 256 // 8
+    assert L.pkv_decode_workspace_bytes(32, 64, 4096, 0, ctypes.byref(d)) == \
+        L.pkv_decode_workspace_bytes(32, 64, 4096, w, ctypes.byref(d))
 
 
 def test_append_rejects():

@@ -93,12 +93,50 @@ def test_poison_does_not_leak_bitwise():
 
 
 def test_split_count_independence():
+    # One workgroup per KV head (every sequence whole, no merge) against
+    # splits that cut sequences into up to hundreds of pieces.
     b = synth.cfg2(B=6)
     cache, q, tab, lens, mx = decode_state(b)
-    base = run_decode(cache, q, tab, lens, mx, b.shape.scale, partition_tokens=4096)
-    for pt in (64, 256, 0):
-        o = run_decode(cache, q, tab, lens, mx, b.shape.scale, partition_tokens=pt)
-        assert float((o - base).abs().max()) <= 1e-6
+    base = run_decode(cache, q, tab, lens, mx, b.shape.scale, num_splits=1)
+    ref = oracle.decode(b.q, b.k, b.v, b.lens, b.shape.scale)
+    assert max_err(base, ref) <= TOL["bf16"]
+    for ns in (2, 3, 17, 128, 1000, 0):
+        o = run_decode(cache, q, tab, lens, mx, b.shape.scale, num_splits=ns)
+        assert float((o - base).abs().max()) <= 1e-5, ns
+
+
+def test_empty_and_tiny_sequences_between_long_ones():
+    # Empty sequences inside the batch, and ranges that hold several whole
+    # short sequences plus pieces of long ones.
+    lens = [0, 3000, 1, 0, 17, 2000, 0, 33, 5, 0]
+    b = synth.custom_decode(12, [max(L, 1) for L in lens], Hq=64, Hkv=8, D=128, dtype="bf16",
+                            block_size=16)
+    cache, q, tab, lens_d, mx = decode_state(b)
+    for i, L in enumerate(lens):
+        if L == 0:
+            lens_d[i] = 0
+    for ns in (1, 7, 64, 0):
+        out = run_decode(cache, q, tab, lens_d, mx, b.shape.scale, num_splits=ns)
+        for i, L in enumerate(lens):
+            if L == 0:
+                assert torch.count_nonzero(out[i]) == 0
+        keep = [i for i, L in enumerate(lens) if L > 0]
+        st = b.seq_start()
+        kk = np.concatenate([b.k[st[i]:st[i + 1]] for i in keep])
+        vv = np.concatenate([b.v[st[i]:st[i + 1]] for i in keep])
+        ref = oracle.decode(b.q[keep], kk, vv, b.lens[keep], b.shape.scale)
+        assert max_err(out[keep], ref) <= TOL["bf16"], ns
+
+
+def test_batch_above_one_launch():
+    # More sequences than one launch takes (1024): the call splits the batch.
+    g = np.random.default_rng(13)
+    lens = g.integers(1, 40, size=1100)
+    b = synth.custom_decode(13, lens, Hq=8, Hkv=8, D=64, dtype="f32", block_size=16)
+    cache, q, tab, lens_d, mx = decode_state(b)
+    out = run_decode(cache, q, tab, lens_d, mx, b.shape.scale)
+    ref = oracle.decode(b.q, b.k, b.v, b.lens, b.shape.scale)
+    assert max_err(out, ref) <= TOL["f32"]
 
 
 def test_length_one_returns_v_exactly():
@@ -149,3 +187,24 @@ def test_out_of_range_block_id_contributes_nothing():
     keep = np.r_[0:16, 32:64]
     ref = oracle.decode(b.q, b.k[keep], b.v[keep], [48], b.shape.scale)
     assert max_err(out, ref) <= TOL["bf16"]
+
+
+def test_workspace_reused_across_calls():
+    # One workspace serves calls of different batches and split counts back
+    # to back: nothing a call leaves in it changes the next call's result.
+    import paged_kv_cache_indirected_amd as pkv
+    b1 = synth.cfg2(B=6)
+    b2 = synth.custom_decode(14, [700, 5, 1300], Hq=64, Hkv=8, D=128, dtype="bf16",
+                             block_size=16)
+    st1, st2 = decode_state(b1), decode_state(b2)
+    ws = torch.zeros(pkv.decode_workspace_bytes(6, 64, 4096, st1[0].desc, 1000),
+                     dtype=torch.uint8, device="cuda")
+    r1 = oracle.decode(b1.q, b1.k, b1.v, b1.lens, b1.shape.scale)
+    r2 = oracle.decode(b2.q, b2.k, b2.v, b2.lens, b2.shape.scale)
+    for ns in (7, 64, 3, 1000, 0):
+        for (cache, q, tab, lens, mx), ref in ((st1, r1), (st2, r2)):
+            out = torch.empty(tuple(q.shape), dtype=torch.float32, device="cuda")
+            pkv.decode(q, cache.k_cache, cache.v_cache, tab, lens, b1.shape.scale, out, cache.desc,
+                       mx, workspace=ws, num_splits=ns)
+            torch.cuda.synchronize()
+            assert max_err(out, ref) <= TOL["bf16"], ns
