@@ -1,20 +1,28 @@
 #!/usr/bin/env python3
-"""Benchmark of the paged-KV decode step on one MI355X.
+"""Benchmark of the paged-KV attention path on one MI355X.
 
-Workload: the Llama-70B-shaped layer (64 query / 8 KV heads, head_dim 128,
-bf16, 16-token blocks, 32 sequences with context U[512, 4096], physical
-blocks shuffled over a pool 1.2x the need).  One step = the slot-mapped append
-of each sequence's current token (pkv_append) + paged decode attention over
-its whole context (pkv_decode).  Inputs are resident in HBM before timing.
-To keep the 256 MB Infinity Cache from serving repeated reads of the ~300 MB
-of K/V, R copies of the paged state (each with its own block placement) are
-rotated so that R * pool exceeds 1 GB.
+Headline workload: the Llama-70B-shaped layer (64 query / 8 KV heads,
+head_dim 128, bf16, 16-token blocks, 32 sequences with context U[512, 4096],
+physical blocks shuffled over a pool 1.2x the need).  One step = the
+slot-mapped append of each sequence's current token (pkv_append) + paged
+decode attention over its whole context (pkv_decode).  Inputs are resident in
+HBM before timing.  To keep the 256 MB Infinity Cache from serving repeated
+reads of the ~300 MB of K/V, R copies of the paged state (each with its own
+block placement) are rotated so that R * pool exceeds 1 GB.
 
-Prints one JSON line (rank 0, N = 1).
+The other workloads are measured in the same run and reported under
+"workloads": the continuous-batching step (256 sequences, 32-token blocks,
+churn between steps), prefix-sharing decode (128 sequences on one 2048-token
+shared prefix), chunked prefill on MFMA mixed with decode, plus the
+bandwidth probes that bound the gather (contiguous read, paged tile read).
+
+Prints one JSON line (N = 1).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -27,37 +35,71 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode effective KV GB/s (% of HBM peak) + seq-steps/s, 64q/8kv hd128"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_cfg2_pmc_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_indirected_amd", "csrc", "decode.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_copies(batch, copies: int):
-    """R independent paged states of the same logical batch."""
-    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+def kv_row_bytes(sh):
+    return sh.Hkv * sh.D * 2 * sh.elem
+
+
+class Timer:
+    """HIP events on the current (launch) stream around n calls of fn."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+
+    def per_call(self, fn, n, warmup=3):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record()
+            fn()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3   # seconds
+
+
+def paged_state(batch, pool_seed, device="cuda"):
+    """One paged copy of a decode batch: every row but each sequence's last
+    loaded through the pool and pkv_append; the step's last token is left for
+    the timed append.  Returns a dict of device tensors."""
+    import torch
     import paged_kv_cache_indirected_amd as pkv
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
     sh = batch.shape
     st = batch.seq_start()
     ids = list(range(batch.B))
+    dt = pkv.F32 if sh.dtype == "f32" else pkv.BF16
+    cache = PagedCache(batch.pool_blocks, sh.Hkv, sh.block_size, sh.D, dt, pool_seed=pool_seed)
     rows_k = np.concatenate([batch.k[st[b]:st[b + 1] - 1] for b in ids])
     rows_v = np.concatenate([batch.v[st[b]:st[b + 1] - 1] for b in ids])
+    cache.add_sequences(ids, batch.lens - 1, rows_k, rows_v)
+    slots = cache.seqs.append_batch(ids)            # the step's bookkeeping (host)
+    tables, lens, max_len = cache.tables(ids)
     last = st[1:] - 1
-    states = []
-    for r in range(copies):
-        cache = PagedCache(batch.pool_blocks, sh.Hkv, sh.block_size, sh.D, pkv.BF16,
-                           pool_seed=batch.pool_seed + 7919 * r)
-        cache.add_sequences(ids, batch.lens - 1, rows_k, rows_v)
-        slots = cache.seqs.append_batch(ids)            # the step's bookkeeping (host)
-        tables, lens, max_len = cache.tables(ids)
-        import torch
-        states.append(dict(
-            cache=cache, tables=tables, lens=lens, max_len=max_len,
-            slots=torch.from_numpy(slots).to("cuda"),
-            k_new=to_device_rows(batch.k[last], pkv.BF16, "cuda"),
-            v_new=to_device_rows(batch.v[last], pkv.BF16, "cuda"),
-        ))
-    return states
+    return dict(cache=cache, tables=tables, lens=lens, max_len=max_len,
+                slots=torch.from_numpy(slots).to(device),
+                k_new=to_device_rows(batch.k[last], dt, device),
+                v_new=to_device_rows(batch.v[last], dt, device),
+                q=to_device_rows(batch.q, dt, device))
+
+
+def workspace(B, Hq, max_len, desc, splits):
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    n = pkv.decode_workspace_bytes(B, Hq, max_len, desc, splits)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
 
 
 def cpu_baseline(batch, min_seconds: float = 10.0, max_reps: int = 400):
@@ -75,17 +117,290 @@ def cpu_baseline(batch, min_seconds: float = 10.0, max_reps: int = 400):
         el = time.perf_counter() - t0
         if el >= min_seconds or reps >= max_reps:
             break
-    sh = batch.shape
-    step_bytes = float(batch.lens.sum()) * sh.Hkv * sh.D * 2 * sh.elem
+    step_bytes = float(batch.lens.sum()) * kv_row_bytes(batch.shape)
     try:
         model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if "model name" in l][0]
     except Exception:
         model = "unknown"
-    return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads,
+    return {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"whole decode step (B={batch.B}, all {batch.B * sh.Hq} (seq, head) rows) "
-                      f"x {reps} repetitions, {el:.1f} s, fp64, cpu: {model}",
-            "seq_steps_per_s": batch.B * reps / el}
+            "sample": f"whole decode step of the Llama-70B-shaped batch (B={batch.B}, all "
+                      f"{batch.B * batch.shape.Hq} (seq, head) rows, {int(batch.lens.sum())} "
+                      f"context tokens) x {reps} repetitions in {el:.1f} s, fp64, cpu: {model}",
+            "seq_steps_per_s": round(batch.B * reps / el, 2)}
+
+
+def pmc_traffic(launch_bytes):
+    """HBM bytes per decode call from the committed PMC summary, if it was
+    taken on the current decode source; else None."""
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("decode_hip_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+# ---------------------------------------------------------------------------
+# Workloads beyond the headline (reported under "workloads").
+
+def bench_probes(timer):
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_indirected_amd", "libpkv_probe.so"))
+    P = ctypes.c_void_p
+    lib.pkv_probe_stream_read.argtypes = [P, ctypes.c_size_t, P, ctypes.c_int, P]
+    lib.pkv_probe_tile_read.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int, P, ctypes.c_int, P]
+    st = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    n = 2 << 30
+    buf = torch.zeros(n // 2, dtype=torch.int16, device="cuda")
+    t = timer.per_call(lambda: lib.pkv_probe_stream_read(buf.data_ptr(), n // 16,
+                                                         sink.data_ptr(), 2048, st), 20)
+    del buf
+    return {"stream_read_GBps": round(n / float(np.median(t)) / 1e9, 1),
+            "note": "contiguous read of 2 GiB, 2048 workgroups"}, lib, sink
+
+
+def bench_tile_probe(lib, sink, states, sh, kv_bytes, timer):
+    """The decode's access shape without arithmetic: whole (block, head)
+    tiles of K and V of the same shuffled pools, in sequence order."""
+    import torch
+    st = torch.cuda.current_stream().cuda_stream
+    lists = []
+    for s in states:
+        tab = s["tables"].cpu().numpy()
+        lens = s["lens"].cpu().numpy()
+        ids = []
+        for b in range(len(lens)):
+            nb = (int(lens[b]) + sh.block_size - 1) // sh.block_size
+            for blk in tab[b, :nb]:
+                ids.extend(int(blk) * sh.Hkv + g for g in range(sh.Hkv))
+        lists.append(torch.tensor(ids, dtype=torch.int64, device="cuda"))
+    tile = sh.block_size * sh.D * sh.elem
+    i = [0]
+
+    def run():
+        s = states[i[0] % len(states)]
+        t = lists[i[0] % len(states)]
+        i[0] += 1
+        lib.pkv_probe_tile_read(s["cache"].k_cache.data_ptr(), s["cache"].v_cache.data_ptr(),
+                                t.data_ptr(), t.numel(), tile, sink.data_ptr(), 4096, st)
+    t = timer.per_call(run, 40)
+    return round(kv_bytes / float(np.median(t)) / 1e9, 1)
+
+
+def bench_cfg3(timer, steps, splits):
+    """Continuous-batching steps: 256 sequences, 32-token blocks; each step
+    appends one token per sequence and decodes; between steps 10% of the
+    sequences finish and are replaced (host bookkeeping + untimed fill)."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    import synth
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    b0 = synth.cfg3_initial()
+    sh = b0.shape
+    st = b0.seq_start()
+    cache = PagedCache(b0.pool_blocks, sh.Hkv, sh.block_size, sh.D, pkv.BF16,
+                       pool_seed=b0.pool_seed)
+    ids = list(range(b0.B))
+    rows_k = np.concatenate([b0.k[st[b]:st[b + 1] - 1] for b in ids])
+    rows_v = np.concatenate([b0.v[st[b]:st[b + 1] - 1] for b in ids])
+    cache.add_sequences(ids, b0.lens - 1, rows_k, rows_v)
+    del rows_k, rows_v
+    next_id = b0.B
+    stride = (8192 + 1 + steps + sh.block_size) // sh.block_size + 1
+    out = torch.empty((b0.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+    ws = workspace(b0.B, sh.Hq, stride * sh.block_size, cache.desc, splits)
+    times, kvb = [], 0.0
+    for step in range(1, steps + 1):
+        slots = torch.from_numpy(cache.seqs.append_batch(ids)).to("cuda")
+        kn, vn, qn = synth.cfg3_step_rows(step, b0.B, sh)
+        kn, vn, qn = (to_device_rows(x, pkv.BF16, "cuda") for x in (kn, vn, qn))
+        tab, lens, mx = cache.tables(ids, stride)
+
+        def run():
+            pkv.append(kn, vn, slots, cache.k_cache, cache.v_cache, cache.desc)
+            pkv.decode(qn, cache.k_cache, cache.v_cache, tab, lens, sh.scale, out, cache.desc, mx,
+                       workspace=ws, num_splits=splits)
+        times.append(float(np.median(timer.per_call(run, 5, warmup=1))))
+        kvb += float(lens.sum().item()) * kv_row_bytes(sh)
+        ev = synth.cfg3_churn(step, b0.B, sh)
+        for i, pos in enumerate(ev.finished):
+            cache.release(ids[pos])
+            ids[pos] = next_id
+            cache.add_sequences([next_id], [int(ev.new_lens[i])], ev.new_k[i], ev.new_v[i])
+            next_id += 1
+    t = float(np.sum(times))
+    return {"workload": "continuous-batching step: append 1 token + decode, B=256, 64q/8kv, "
+                        "d128, bf16, block 32, log-normal context (median 1024), 10% churn/step",
+            "steps": steps, "ms_per_step": round(1e3 * t / steps, 4),
+            "kv_GBps": round(kvb / t / 1e9, 1),
+            "seq_steps_per_s": round(b0.B * steps / t, 1),
+            "pct_of_hbm_peak": round(100 * kvb / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def bench_cfg4(timer, splits):
+    """Prefix-sharing decode: 128 sequences share one 2048-token prefix's
+    physical blocks; logical bytes count the prefix once per sequence."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    import synth
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    b = synth.cfg4()
+    sh = b.shape
+    st = b.seq_start()
+    P = b.prefix_len
+    cache = PagedCache(b.pool_blocks, sh.Hkv, sh.block_size, sh.D, pkv.BF16,
+                       pool_seed=b.pool_seed)
+    cache.add_sequences([-1], [P], b.k[:P], b.v[:P])
+    for s in range(b.B):
+        cache.add_shared(s, -1, P)
+        cache.extend(s, b.k[st[s] + P:st[s + 1]], b.v[st[s] + P:st[s + 1]])
+    tab, lens, mx = cache.tables(list(range(b.B)))
+    q = to_device_rows(b.q, pkv.BF16, "cuda")
+    out = torch.empty((b.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+    ws = workspace(b.B, sh.Hq, mx, cache.desc, splits)
+    t = float(np.median(timer.per_call(
+        lambda: pkv.decode(q, cache.k_cache, cache.v_cache, tab, lens, sh.scale, out, cache.desc,
+                           mx, workspace=ws, num_splits=splits), 30)))
+    logical = float(b.lens.sum()) * kv_row_bytes(sh)
+    unique = float(P + (b.lens - P).sum()) * kv_row_bytes(sh)
+    return {"workload": "prefix-sharing decode: B=128 on one shared 2048-token prefix + "
+                        "U[64,512] private, 64q/8kv, d128, bf16, block 16",
+            "ms_per_call": round(1e3 * t, 4),
+            "logical_kv_GBps": round(logical / t / 1e9, 1),
+            "unique_kv_GBps": round(unique / t / 1e9, 1),
+            "seq_steps_per_s": round(b.B / t, 1),
+            "note": "logical bytes read the shared prefix once per sequence; repeated prefix "
+                    "tiles are served from L2/Infinity Cache, so logical GB/s can exceed HBM"}
+
+
+def bench_cfg5(timer, splits):
+    """Chunked prefill (4 x 512-token causal chunks on MFMA) in the same step
+    as 64 decode sequences."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    import synth
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    pre, dec = synth.cfg5()
+    sh = pre.shape
+    pc = PagedCache(pre.pool_blocks, sh.Hkv, sh.block_size, sh.D, pkv.BF16,
+                    pool_seed=pre.pool_seed)
+    ids = list(range(len(pre.chunk)))
+    lsum = pre.prior + pre.chunk
+    qs0 = np.concatenate([[0], np.cumsum(lsum)])
+    prior_k = np.concatenate([pre.k[qs0[s]:qs0[s] + pre.prior[s]] for s in ids])
+    prior_v = np.concatenate([pre.v[qs0[s]:qs0[s] + pre.prior[s]] for s in ids])
+    pc.add_sequences(ids, pre.prior, prior_k, prior_v)
+    chunk_slots = np.concatenate([pc.seqs.append(s, int(pre.chunk[s])) for s in ids])
+    ck = to_device_rows(np.concatenate([pre.k[qs0[s] + pre.prior[s]:qs0[s + 1]] for s in ids]),
+                        pkv.BF16, "cuda")
+    cv = to_device_rows(np.concatenate([pre.v[qs0[s] + pre.prior[s]:qs0[s + 1]] for s in ids]),
+                        pkv.BF16, "cuda")
+    cslots = torch.from_numpy(chunk_slots.astype(np.int32)).to("cuda")
+    ptab, plens, pmx = pc.tables(ids)
+    pq = to_device_rows(pre.q, pkv.BF16, "cuda")
+    qsl = torch.from_numpy(pre.query_start.astype(np.int32)).to("cuda")
+    pout = torch.empty(tuple(pq.shape), dtype=torch.float32, device="cuda")
+    ds = paged_state(dec, dec.pool_seed)
+    dout = torch.empty((dec.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+    dc = ds["cache"]
+    ws = workspace(dec.B, sh.Hq, ds["max_len"], dc.desc, splits)
+    C = int(pre.chunk.max())
+
+    def prefill():
+        pkv.prefill_chunk(pq, qsl, pc.k_cache, pc.v_cache, ptab, plens, sh.scale, pout, pc.desc,
+                          C, pmx)
+
+    def decode():
+        pkv.decode(ds["q"], dc.k_cache, dc.v_cache, ds["tables"], ds["lens"], sh.scale, dout,
+                   dc.desc, ds["max_len"], workspace=ws, num_splits=splits)
+
+    def step():
+        pkv.append(ck, cv, cslots, pc.k_cache, pc.v_cache, pc.desc)
+        pkv.append(ds["k_new"], ds["v_new"], ds["slots"], dc.k_cache, dc.v_cache, dc.desc)
+        prefill()
+        decode()
+    t_pre = float(np.median(timer.per_call(prefill, 10)))
+    t_dec = float(np.median(timer.per_call(decode, 20)))
+    t_step = float(np.median(timer.per_call(step, 10)))
+    flops = sum(4.0 * sh.Hq * sh.D * (int(c) * int(p) + int(c) * (int(c) + 1) / 2)
+                for p, c in zip(pre.prior, pre.chunk))
+    dbytes = float(dec.lens.sum()) * kv_row_bytes(sh)
+    return {"workload": "chunked prefill mixed with decode: 4 x 512-token causal chunks over "
+                        "prior U[0,7680] (MFMA) + 64 decode seqs U[256,8192], 64q/8kv, d128, "
+                        "bf16, block 16",
+            "prior_tokens": [int(x) for x in pre.prior],
+            "prefill_ms": round(1e3 * t_pre, 4),
+            "prefill_TFLOPs": round(flops / t_pre / 1e12, 1),
+            "prefill_mfma_frac": round(flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "prefill_algorithmic_GFLOP": round(flops / 1e9, 2),
+            "decode_ms": round(1e3 * t_dec, 4),
+            "decode_kv_GBps": round(dbytes / t_dec / 1e9, 1),
+            "step_ms": round(1e3 * t_step, 4),
+            "step_note": "append of 2048 chunk rows + 64 decode rows, prefill, decode; "
+                         "one stream"}
+
+
+def probe_copy(nbytes=1 << 30, reps=3):
+    """Run only the plain copy probe (nbytes read + nbytes written per call),
+    so that a hardware-counter run sees a kernel of known traffic."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_indirected_amd", "libpkv_probe.so"))
+    P = ctypes.c_void_p
+    lib.pkv_probe_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int, P]
+    src = torch.zeros(nbytes // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(reps):
+        lib.pkv_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes // 16, 4096, st)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe_copy_bytes": nbytes, "reps": reps}))
+
+
+def _pmc_per_dispatch(csv_path, name_part, counter):
+    import csv
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals, key=int)]
+
+
+def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_path, copy_bytes,
+                kv_bytes):
+    """HBM bytes per decode call from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the same counter reads for the copy probe
+    of known size.  Steady-state dispatches only (the first of each kernel
+    is dropped)."""
+    fk = _pmc_per_dispatch(fetch_csv, "k_decode", "FETCH_SIZE")[1:]
+    fm = _pmc_per_dispatch(fetch_csv, "k_merge", "FETCH_SIZE")[1:]
+    wk = _pmc_per_dispatch(write_csv, "k_decode", "WRITE_SIZE")[1:]
+    wm = _pmc_per_dispatch(write_csv, "k_merge", "WRITE_SIZE")[1:]
+    cf = _pmc_per_dispatch(copy_fetch_csv, "k_copy", "FETCH_SIZE")
+    cw = _pmc_per_dispatch(copy_write_csv, "k_copy", "WRITE_SIZE")
+    sf = copy_bytes / (1024.0 * float(np.median(cf)))
+    sw = copy_bytes / (1024.0 * float(np.median(cw)))
+    fetch = 1024.0 * sf * (float(np.mean(fk)) + float(np.mean(fm)))
+    write = 1024.0 * sw * (float(np.mean(wk)) + float(np.mean(wm)))
+    rec = {
+        "kernel": "pkv_decode call on the Llama-70B-shaped batch (k_decode + k_merge)",
+        "decode_hip_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+        "fetch_KiB_per_dispatch": {"k_decode": float(np.mean(fk)), "k_merge": float(np.mean(fm))},
+        "write_KiB_per_dispatch": {"k_decode": float(np.mean(wk)), "k_merge": float(np.mean(wm))},
+        "copy_probe": {"bytes_each_way": copy_bytes, "fetch_KiB": float(np.median(cf)),
+                       "write_KiB": float(np.median(cw)), "fetch_scale": sf, "write_scale": sw},
+        "hbm_fetch_bytes_per_call": fetch,
+        "hbm_write_bytes_per_call": write,
+        "hbm_bytes_per_call": fetch + write,
+        "algorithmic_bytes_per_call": kv_bytes,
+        "traffic_over_algorithmic": (fetch + write) / kv_bytes,
+    }
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def main():
@@ -94,12 +409,29 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
-    ap.add_argument("--splits", type=int, default=0, help="workgroups per KV head (0: library choice)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode workgroups per KV head (0: library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other workloads and the probes")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="run only the copy probe (for hardware-counter scaling)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                       "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn counter CSVs into the committed per-call traffic summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        import synth
+        b = synth.cfg2()
+        pmc_summary(*args.pmc_summary, PMC_FILE, 1 << 30,
+                    float(b.lens.sum()) * kv_row_bytes(b.shape))
+        return
+    if args.probe_copy:
+        probe_copy()
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the paged-KV path here is single-GPU by design)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the "
+              "paged-KV path here runs on one GPU (no sharding, no collectives)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -107,26 +439,29 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    timer = Timer()
     batch = synth.cfg2()
     sh = batch.shape
-    log(f"[bench] building {args.copies} paged copies of cfg2 (B={batch.B}, "
-        f"sum L={int(batch.lens.sum())}, pool={batch.pool_blocks} blocks)")
-    states = build_copies(batch, args.copies)
-    from paged_kv_cache_indirected_amd.paged import to_device_rows
-    q = to_device_rows(batch.q, pkv.BF16, "cuda")
+    log(f"[bench] building {args.copies} paged copies of the Llama-70B-shaped batch "
+        f"(B={batch.B}, sum L={int(batch.lens.sum())}, pool={batch.pool_blocks} blocks)")
+    states = [paged_state(batch, batch.pool_seed + 7919 * r) for r in range(args.copies)]
     out = torch.empty((batch.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
     desc = states[0]["cache"].desc
     max_len = max(s["max_len"] for s in states)
-    nbytes = pkv.decode_workspace_bytes(batch.B, sh.Hq, max_len, desc, args.splits)
-    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    ws = workspace(batch.B, sh.Hq, max_len, desc, args.splits)
     splits = args.splits or pkv.decode_num_splits(batch.B, sh.Hq, max_len, desc)
+    q = states[0]["q"]
+
+    def decode_call(s):
+        c = s["cache"]
+        pkv.decode(q, c.k_cache, c.v_cache, s["tables"], s["lens"], sh.scale, out, c.desc,
+                   max_len, workspace=ws, num_splits=args.splits)
 
     def step(i):
         s = states[i % len(states)]
         c = s["cache"]
         pkv.append(s["k_new"], s["v_new"], s["slots"], c.k_cache, c.v_cache, c.desc)
-        pkv.decode(q, c.k_cache, c.v_cache, s["tables"], s["lens"], sh.scale, out, c.desc,
-                   max_len, workspace=ws, num_splits=args.splits)
+        decode_call(s)
 
     for i in range(args.warmup):
         step(i)
@@ -140,24 +475,19 @@ def main():
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
 
-    # Decode launches alone, each bracketed by events on the launch stream.
-    n_dec = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_dec)]
-    for i in range(n_dec):
-        s = states[i % len(states)]
-        c = s["cache"]
-        evs[i][0].record()
-        pkv.decode(q, c.k_cache, c.v_cache, s["tables"], s["lens"], sh.scale, out, c.desc,
-                   max_len, workspace=ws, num_splits=args.splits)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    dec_avg = float(dec_ms.mean())
+    # The decode call alone (split kernel + merge kernel), each bracketed by
+    # events on the launch stream.
+    it = [0]
 
-    kv_bytes = float(batch.lens.sum()) * sh.Hkv * sh.D * 2 * sh.elem
+    def one_decode():
+        decode_call(states[it[0] % len(states)])
+        it[0] += 1
+    dec_s = timer.per_call(one_decode, args.steps)
+    dec_avg = float(dec_s.mean())
+
+    kv_bytes = float(batch.lens.sum()) * kv_row_bytes(sh)
     gbs_step = kv_bytes / (ms_step * 1e-3) / 1e9
-    gbs_dec = kv_bytes / (dec_avg * 1e-3) / 1e9
+    gbs_dec = kv_bytes / dec_avg / 1e9
     res = {
         "metric": METRIC,
         "value": round(gbs_step, 1),
@@ -183,18 +513,38 @@ def main():
         "seq_steps_per_s": round(batch.B / (ms_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pkv_decode (balanced split pass + LSE merge)",
+            "kernel": "pkv_decode call (k_decode split pass + k_merge)",
             "achieved": round(gbs_dec, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs_dec / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": pmc_traffic(kv_bytes),
             "algorithmic_bytes_per_launch": int(kv_bytes),
-            "avg_launch_ms": round(dec_avg, 5),
-            "p10_ms": round(float(np.percentile(dec_ms, 10)), 5),
-            "p90_ms": round(float(np.percentile(dec_ms, 90)), 5),
+            "avg_launch_ms": round(1e3 * dec_avg, 5),
+            "p10_ms": round(1e3 * float(np.percentile(dec_s, 10)), 5),
+            "p90_ms": round(1e3 * float(np.percentile(dec_s, 90)), 5),
         },
     }
+    if not args.headline_only:
+        log("[bench] probes")
+        probes, plib, sink = bench_probes(timer)
+        probes["paged_tile_read_GBps"] = bench_tile_probe(plib, sink, states, sh, kv_bytes, timer)
+        probes["paged_tile_note"] = ("the decode's tiles of the same shuffled pools, read with "
+                                     "its access shape and no arithmetic")
+        res["roofline"]["achievable_probes"] = probes
+        res["roofline"]["frac_of_paged_tile_probe"] = round(
+            gbs_dec / probes["paged_tile_read_GBps"], 4)
+        del states
+        torch.cuda.empty_cache()
+        log("[bench] continuous batching")
+        wl = {"continuous_batching": bench_cfg3(timer, 10, args.splits)}
+        torch.cuda.empty_cache()
+        log("[bench] prefix sharing")
+        wl["prefix_sharing"] = bench_cfg4(timer, args.splits)
+        torch.cuda.empty_cache()
+        log("[bench] chunked prefill + decode")
+        wl["chunked_prefill_mixed"] = bench_cfg5(timer, args.splits)
+        res["workloads"] = wl
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(batch)
