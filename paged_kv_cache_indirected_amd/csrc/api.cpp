@@ -50,10 +50,11 @@ int check_heads(int32_t hq, const pkv_cache_desc *c, const char *who)
 }
 
 // Decode split: W workgroups per KV head cut the batch's blocks into equal
-// ranges.  W fills the chip with kGroupsPerCU resident workgroups per CU, but
-// is never larger than gives each of a workgroup's 4 waves 2 blocks of the
-// batch's upper-bound block count.
-constexpr int kGroupsPerCU = 2;
+// ranges.  W = one resident workgroup per CU for the KV heads together
+// (kGroupsPerCU): more ranges only add pieces to merge and per-piece
+// start-up, fewer leave CUs idle.  Measured on the Llama-70B-shaped batch:
+// 32 per KV head 75.8 us, 64 77.4 us, 128 85.6 us per call.
+constexpr int kGroupsPerCU = 1;
 
 int64_t blocks_bound(int32_t num_seqs, int32_t max_ctx, const pkv_cache_desc *c)
 {
@@ -64,10 +65,10 @@ int64_t blocks_bound(int32_t num_seqs, int32_t max_ctx, const pkv_cache_desc *c)
 
 int32_t auto_splits(int32_t num_seqs, int32_t max_ctx, const pkv_cache_desc *c)
 {
-    const int64_t cap = ((int64_t)pkv::device_cu_count() * kGroupsPerCU + c->num_kv_heads - 1) /
-                        c->num_kv_heads;
-    const int64_t want = (blocks_bound(num_seqs, max_ctx, c) + 7) / 8;
-    int64_t w = want < cap ? want : cap;
+    (void)num_seqs;
+    (void)max_ctx;
+    int64_t w = ((int64_t)pkv::device_cu_count() * kGroupsPerCU + c->num_kv_heads - 1) /
+                c->num_kv_heads;
     w = w < 1 ? 1 : (w > 65535 ? 65535 : w);
     return (int32_t)w;
 }

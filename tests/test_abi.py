@@ -90,11 +90,11 @@ def test_workspace_size_rules():
         assert n >= (bc + 1) * 4 + pieces * 64 * 128 * 4 + pieces * 64 * 2 * 4
     assert L.pkv_decode_workspace_bytes(0, 64, 1000, 8, ctypes.byref(d)) == 0
     assert L.pkv_decode_workspace_bytes(4, 64, 1000, -1, ctypes.byref(d)) == 0
-    # Library choice: at least 1, at most 65535, and no more than gives each
-    # of a workgroup's 4 waves 2 blocks of the batch's upper-bound block count.
-    assert L.pkv_decode_num_splits(1, 64, 16, ctypes.byref(d)) == 1
+    # Library choice: one workgroup per CU over the KV heads (256 CUs when no
+    # device can be queried), independent of the batch.
     w = L.pkv_decode_num_splits(32, 64, 4096, ctypes.byref(d))
-    assert 1 <= w <= 32 * 256 // 8
+    assert 1 <= w <= 65535
+    assert w == L.pkv_decode_num_splits(1, 64, 16, ctypes.byref(d))
     assert L.pkv_decode_workspace_bytes(32, 64, 4096, 0, ctypes.byref(d)) == \
         L.pkv_decode_workspace_bytes(32, 64, 4096, w, ctypes.byref(d))
 
