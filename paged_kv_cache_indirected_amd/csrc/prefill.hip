@@ -52,6 +52,8 @@ constexpr int kThreads = NW * 64;
 constexpr int KT = 64;                 // keys per tile
 constexpr int ROWS = NW * 32;          // query rows per workgroup (32 per wave)
 constexpr float kLazyMax = 8.0f;       // running-max slack, log2 units
+constexpr int kIdChunk = 1024;         // block ids staged in LDS at a time
+constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data format, no swizzle
 
 template <int D>
 struct PShape {
@@ -76,12 +78,22 @@ struct PArgs {
     const int32_t *lens;
     void *out;
     int32_t stride, Hq, Hkv, num_blocks, n_qtiles, out_dtype;
+    int32_t S;                        // sequences in the launch
     float scale_log2;
 };
 
 // LDS column of key kk (0..63) in the transposed V tile: the 8 keys a lane
 // feeds to one PV MFMA, {32s + 4q + i} and {32s + 16 + 4q + i} for i < 4,
 // sit next to each other.
+// Element offset of key position pos in row d of the transposed V tile:
+// 16-byte units are XOR-swizzled by the row's eighth, so the 16 rows that one
+// store instruction writes (d = 8 cc + e) fall on different LDS banks while a
+// lane's 8-key MFMA operand stays one aligned 16-byte read.
+__device__ __forceinline__ int vcol(int d, int pos)
+{
+    return (((pos >> 3) ^ ((d >> 3) & 7)) << 3) | (pos & 7);
+}
+
 __device__ __forceinline__ int vpos(int kk)
 {
     return (kk & 32) | ((kk >> 2) & 3) << 3 | ((kk >> 4) & 1) << 2 | (kk & 3);
@@ -109,6 +121,25 @@ __device__ __forceinline__ uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+// Combine v with lane (l ^ X) (X = 16 or 32) by max; both lanes get the
+// same bits.
+template <int X>
+__device__ __forceinline__ float xmax(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    auto p = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+template <int X>
+__device__ __forceinline__ float xsum(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    auto p = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+}
+
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
 {
@@ -116,16 +147,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     constexpr int TQ = ROWS / G;                     // chunk tokens per workgroup
     constexpr int NDS = Sh::NDS, NDT = Sh::NDT, CPR = Sh::CPR, VK = Sh::VK;
     constexpr int KSTR = Sh::KSTR, VSTR = Sh::VSTR;
+    constexpr int IDS = kIdChunk;                    // block ids staged per chunk
+    constexpr int CT = IDS * BS / KT;                // key tiles per id chunk
 
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][Sh::KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][Sh::VBUF];
+    __shared__ int32_t lds_ids[IDS];
 
     const int g = blockIdx.x;
     const int qt = a.n_qtiles - 1 - (int)blockIdx.y;
-    const int s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, quad = lane >> 4;
+
+    // Sequences are taken longest context first (grid z is the rank), so the
+    // heaviest workgroups start first and the light ones fill the tail.
+    // Ranking is done for up to 64 sequences; beyond that, in order.
+    int s = blockIdx.z;
+    if (a.S <= 64) {
+        const int i = lane < a.S ? lane : 0;
+        const int wi = a.lens[i];
+        int rank = 0;
+        for (int j = 0; j < a.S; ++j) {
+            const int wj = __builtin_amdgcn_readlane(wi, j);
+            rank += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.S && rank == (int)blockIdx.z);
+        s = hit ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit)) : blockIdx.z;
+    }
 
     const int q0 = a.qsl[s];
     const int C = a.qsl[s + 1] - q0;
@@ -157,46 +206,86 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     const int wtok = tok0 + (w * 32) / G;
     const int lim_w = wtok < tok_end ? p0 + wtok : 0x7FFFFFFF;
 
+    // Scores enter the exponent as fma(s, c, -m) with c = |scale| log2(e):
+    // for a negative scale the q operand's sign bits are flipped (exact), so
+    // the running max of s * c is c times the max of the raw scores.
+    // (c is kept away from 0 so that masked -inf scores still give 0.)
+    const float c = fmaxf(a.scale_log2 < 0.0f ? -a.scale_log2 : a.scale_log2, 1e-30f);
+    const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
     bf16x8 qf[2][NDS];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (valid[ct])
+            if (valid[ct]) {
                 v = *reinterpret_cast<const uint4 *>(a.q + qrow[ct] + ds * 32 + quad * 8);
+                v.x ^= qsign;
+                v.y ^= qsign;
+                v.z ^= qsign;
+                v.w ^= qsign;
+            }
             qf[ct][ds] = __builtin_bit_cast(bf16x8, v);
         }
 
     const int32_t *bt = a.tables + (int64_t)s * a.stride;
     const int64_t hstride = (int64_t)BS * D;         // elements per (block, head) tile
     const int64_t bstride = (int64_t)a.Hkv * hstride;
+    const uint16_t *kg = a.kc + g * hstride;
+    const uint16_t *vg = a.vc + g * hstride;
+    const int nblk = (kend + BS - 1) / BS;           // blocks the workgroup reads
+
+    // Block ids of the key range staged through LDS, IDS at a time.
+    auto stage_ids = [&](int chunk) {
+        for (int i = tid; i < IDS; i += kThreads) {
+            const int jb = chunk * IDS + i;
+            lds_ids[i] = jb < nblk ? bt[jb] : -1;
+        }
+    };
 
     uint4 kst[Sh::KLD], vst[VK];
-    // Global loads of key tile kt into registers.
+    // Global loads of key tile kt into registers.  With this thread mapping
+    // every load of a wave falls in one block (the block index is
+    // wave-uniform for all supported shapes), so each load goes through a
+    // buffer resource on that block's (block, head) tile held in scalar
+    // registers; a block id outside the pool, or a block past the context,
+    // gets an empty resource and reads zeros without touching memory.
+    auto tile_rsrc = [&](const uint16_t *base, int j) {
+        const int jj = __builtin_amdgcn_readfirstlane(j);
+        const int id = jj < L ? lds_ids[(jj / BS) % IDS] : -1;
+        const int ids = __builtin_amdgcn_readfirstlane(id);
+        const bool ok = (unsigned)ids < (unsigned)a.num_blocks;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(base + (ok ? (int64_t)ids * bstride : 0)), 0,
+            ok ? (int)(hstride * 2) : 0, kRsrcWord3);
+    };
     auto load_tile = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < Sh::KLD; ++i) {
-            const int c = tid + kThreads * i;
-            const int kk = c / CPR, cc = c % CPR;
+            const int cidx = tid + kThreads * i;
+            const int kk = cidx / CPR, cc = cidx % CPR;
             const int j = kt * KT + kk;
-            const int id = j < L ? bt[j / BS] : -1;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if ((unsigned)id < (unsigned)a.num_blocks)
-                v = *reinterpret_cast<const uint4 *>(a.kc + id * bstride + g * hstride +
-                                                     (j % BS) * D + cc * 8);
-            kst[i] = v;
+            // Keys past the context inside the last block read as the
+            // block's unused slots; they are masked before use.
+            kst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                tile_rsrc(kg, kt * KT + (w * 64) / CPR + (kThreads / CPR) * i),
+                ((j % BS) * D + cc * 8) * 2, 0, 0));
         }
         const int cc = tid % CPR, k0 = (tid / CPR) * VK;
 #pragma unroll
         for (int e = 0; e < VK; ++e) {
             const int j = kt * KT + k0 + e;
-            const int id = j < L ? bt[j / BS] : -1;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if ((unsigned)id < (unsigned)a.num_blocks)
-                v = *reinterpret_cast<const uint4 *>(a.vc + id * bstride + g * hstride +
-                                                     (j % BS) * D + cc * 8);
-            vst[e] = v;
+            vst[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                tile_rsrc(vg, kt * KT + ((w * 64) / CPR) * VK), ((j % BS) * D + cc * 8) * 2, 0,
+                0));
+        }
+        // Unused slots past the context end must not reach the PV product as
+        // NaN (0 * NaN = NaN): zero them (only the tile holding the end).
+        if (kt * KT + KT > L) {
+#pragma unroll
+            for (int e = 0; e < VK; ++e)
+                if (kt * KT + k0 + e >= L)
+                    vst[e] = make_uint4(0, 0, 0, 0);
         }
     };
     // Registers -> LDS buffer: K as is, V transposed with its keys placed in
@@ -204,14 +293,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < Sh::KLD; ++i) {
-            const int c = tid + kThreads * i;
-            const int kk = c / CPR, cc = c % CPR;
+            const int cidx = tid + kThreads * i;
+            const int kk = cidx / CPR, cc = cidx % CPR;
             *reinterpret_cast<uint4 *>(&lds_k[buf][kk * KSTR + cc * 8]) = kst[i];
         }
         const int cc = tid % CPR, k0 = (tid / CPR) * VK;
-        uint16_t *vt = &lds_v[buf][(cc * 8) * VSTR + vpos(k0)];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+            const int d = cc * 8 + e;
+            uint16_t *vt = &lds_v[buf][d * VSTR + vcol(d, vpos(k0))];
             const int wi = e >> 1;
             if constexpr (VK == 4) {
                 uint2 pr;
@@ -219,9 +309,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
                                : lo_pair(word(vst[0], wi), word(vst[1], wi));
                 pr.y = (e & 1) ? hi_pair(word(vst[2], wi), word(vst[3], wi))
                                : lo_pair(word(vst[2], wi), word(vst[3], wi));
-                *reinterpret_cast<uint2 *>(vt + e * VSTR) = pr;
+                *reinterpret_cast<uint2 *>(vt) = pr;
             } else {
-                *reinterpret_cast<uint32_t *>(vt + e * VSTR) =
+                *reinterpret_cast<uint32_t *>(vt) =
                     (e & 1) ? hi_pair(word(vst[0], wi), word(vst[1], wi))
                             : lo_pair(word(vst[0], wi), word(vst[1], wi));
             }
@@ -237,6 +327,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
 
     if (NT > 0) {
+        stage_ids(0);
+        __syncthreads();
         load_tile(0);
         store_tile(0);
     }
@@ -244,8 +336,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
 
     for (int kt = 0; kt < NT; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < NT)
+        if (kt + 1 < NT) {
+            if ((kt + 1) % CT == 0) {                // next tile starts a new id chunk
+                stage_ids((kt + 1) / CT);
+                __syncthreads();
+            }
             load_tile(kt + 1);
+        }
 
         // S^T tile: 64 keys x 32 query columns.
         f32x4 sacc[4][2];
@@ -267,63 +364,72 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
             }
 
         // Online softmax per query column.  Lane holds keys
-        // kt*64 + ks*16 + 4*quad + i of column n.
+        // kt*64 + ks*16 + 4*quad + i of column n.  Only tiles that cross the
+        // causal diagonal or the context end are masked (wave-uniform test,
+        // taken as a real branch).
         const bool full = kt * KT + KT - 1 <= lim_w;
+        if (!full) [[unlikely]] {
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (kt * KT + ks * 16 + quad * 4 + i > lim[ct])
+                            sacc[ks][ct][i] = -INFINITY;
+        }
         bf16x8 phi[2][2], plo[2][2];
         bool grew = false;
         float alpha[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            float x[4][4];
             float mt = -INFINITY;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = sacc[ks][ct][i] * a.scale_log2;
-                    if (!full)
-                        v = (kt * KT + ks * 16 + quad * 4 + i <= lim[ct]) ? v : -INFINITY;
-                    x[ks][i] = v;
-                    mt = fmaxf(mt, v);
-                }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+                mt = fmaxf(mt, fmaxf(fmaxf(sacc[ks][ct][0], sacc[ks][ct][1]),
+                                     fmaxf(sacc[ks][ct][2], sacc[ks][ct][3])));
+            mt = xmax<16>(mt);
+            mt = xmax<32>(mt) * c;
             const bool up = mt > m[ct] + kLazyMax;
             const float mn = up ? mt : m[ct];
             alpha[ct] = up ? __builtin_amdgcn_exp2f(m[ct] - mn) : 1.0f;
             grew |= up;
             m[ct] = mn;
-            const bool dead = (mn == -INFINITY);
+            // exp2(s c - m); a fully masked column so far (m = -inf) gets 0.
+            const float negm = mn == -INFINITY ? 0.0f : -mn;
             float sum = 0.0f;
             float pv[4][4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pv[ks][i] = dead ? 0.0f : __builtin_amdgcn_exp2f(x[ks][i] - mn);
+                    pv[ks][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks][ct][i], c, negm));
                     sum += pv[ks][i];
                 }
             lsum[ct] = __builtin_fmaf(lsum[ct], alpha[ct], sum);
             // P^T operands for the two 32-key k-steps: keys {32s + 4q + i}
-            // then {32s + 16 + 4q + i}; hi part and the rounding remainder.
+            // then {32s + 16 + 4q + i}.  hi = p truncated to bf16 (its top
+            // 16 bits, exact as an fp32 value), lo = bf16(p - hi): together
+            // they carry ~16 significant bits of p.
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                bf16x8 h, lo;
+                uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int i = 0; i < 4; i += 2) {
-                        const float p0v = pv[2 * s2 + half][i], p1v = pv[2 * s2 + half][i + 1];
-                        const bf16x2_t hp = __builtin_convertvector(f32x2{p0v, p1v}, bf16x2_t);
-                        const float r0 = p0v - (float)hp[0], r1 = p1v - (float)hp[1];
-                        const bf16x2_t lp = __builtin_convertvector(f32x2{r0, r1}, bf16x2_t);
-                        h[half * 4 + i] = hp[0];
-                        h[half * 4 + i + 1] = hp[1];
-                        lo[half * 4 + i] = lp[0];
-                        lo[half * 4 + i + 1] = lp[1];
+                        const uint32_t u0 = __builtin_bit_cast(uint32_t, pv[2 * s2 + half][i]);
+                        const uint32_t u1 = __builtin_bit_cast(uint32_t, pv[2 * s2 + half][i + 1]);
+                        const float r0 = pv[2 * s2 + half][i] -
+                                         __builtin_bit_cast(float, u0 & 0xFFFF0000u);
+                        const float r1 = pv[2 * s2 + half][i + 1] -
+                                         __builtin_bit_cast(float, u1 & 0xFFFF0000u);
+                        hw[half * 2 + i / 2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                        lw[half * 2 + i / 2] = __builtin_bit_cast(
+                            uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2_t));
                     }
-                phi[ct][s2] = h;
-                plo[ct][s2] = lo;
+                phi[ct][s2] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                plo[ct][s2] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
             }
         }
         if (__builtin_amdgcn_ballot_w64(grew) != 0) {
@@ -340,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
-                    &lds_v[buf][(dt * 16 + n) * VSTR + 32 * s2 + 8 * quad]);
+                    &lds_v[buf][(dt * 16 + n) * VSTR + vcol(dt * 16 + n, 32 * s2 + 8 * quad)]);
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct][s2], o[dt][ct],
@@ -359,8 +465,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
         float l = lsum[ct];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        l = xsum<16>(l);
+        l = xsum<32>(l);
         if (!valid[ct])
             continue;
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -430,6 +536,7 @@ int launch_prefill(const PrefillLaunch &p)
     a.Hkv = p.num_kv_heads;
     a.num_blocks = p.num_blocks;
     a.n_qtiles = (int32_t)nqt;
+    a.S = p.num_seqs;
     a.out_dtype = p.out_dtype;
     a.scale_log2 = p.scale * 1.4426950408889634f;
     hipStream_t st = reinterpret_cast<hipStream_t>(p.stream);
