@@ -133,6 +133,29 @@ int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
                const pkv_cache_desc *c, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Decode step with the append fused into the same launch.
+ *
+ * Same result, cache contents included, as
+ *     pkv_append(k_new, v_new, slot_mapping, num_seqs, k_cache, v_cache, c)
+ *     pkv_decode(q, k_cache, ..., context_lens, num_seqs, ...)
+ * for a decode step in which sequence b appends one token (row b of k_new,
+ * v_new: [num_seqs][num_kv_heads][head_dim]) at slot slot_mapping[b], and
+ * that token is position context_lens[b] - 1 of the sequence (the slot the
+ * block table maps that position to: a precondition).  A negative slot
+ * appends nothing, and position L - 1 is then read from the cache.  The new
+ * rows are written to the cache and, for the attention, taken from k_new /
+ * v_new directly, so nothing in the launch reads what it writes.  One launch
+ * fewer per step than the two calls ([KV-prep] "The KV cache": append, then
+ * attend).  Other arguments, workspace and return codes as pkv_decode.
+ */
+int pkv_append_decode(const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                      const void *q, void *k_cache, void *v_cache, const int32_t *block_tables,
+                      int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t max_context_len, float scale, void *out,
+                      int32_t out_dtype, int32_t num_splits, void *workspace,
+                      size_t workspace_bytes, const pkv_cache_desc *c, void *stream);
+
+/* ------------------------------------------------------------------------
  * Causal chunked prefill ([KV-prep] "Chunked prefill": a prompt is split into
  * fixed-size chunks, e.g. 512 tokens, interleaved with decode; the split does
  * not change the result).

@@ -68,6 +68,8 @@ _sig("pkv_decode_num_splits", _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, ctypes.c_float, _P,
      _i32, _i32, _P, _sz, _DESC, _P)
+_sig("pkv_append_decode", ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32,
+     ctypes.c_float, _P, _i32, _i32, _P, _sz, _DESC, _P)
 _sig("pkv_prefill_workspace_bytes", _sz, _i32, _i32, _i32, _DESC)
 _sig("pkv_prefill_chunk", ctypes.c_int, _P, _P, _i32, _i32, _P, _P, _P, _i32, _P, _i32, _i32,
      ctypes.c_float, _P, _i32, _P, _sz, _DESC, _P)
@@ -228,6 +230,36 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, d
                          int(num_splits), _dev(workspace, "workspace"), ws_bytes,
                          ctypes.byref(desc.c()), _stream(stream))
     _check(rc, "pkv_decode")
+
+
+def append_decode(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,
+                  scale: float, out, desc: CacheDesc, max_context_len: int, workspace=None,
+                  num_splits: int = 0, stream=None) -> None:
+    """pkv_append_decode: a decode step's append (one row per sequence) and
+    the decode, in one launch (plus the merge pass)."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    _need(D == desc.head_dim and _dtype_code(q) == desc.dtype, "q must be [B][Hq][head_dim]")
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    row = desc.num_kv_heads * desc.head_dim
+    _need(k_new.numel() == B * row and v_new.numel() == B * row, "k_new/v_new must be [B][Hkv][D]")
+    _need(_dtype_code(k_new) == desc.dtype and _dtype_code(v_new) == desc.dtype, "k_new/v_new dtype")
+    _need(slot_mapping.numel() >= B, "slot_mapping must hold B entries")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] >= B, "block_tables must be [B][W]")
+    _need(context_lens.numel() >= B, "context_lens must hold B entries")
+    _cache_ok(k_cache, desc, "k_cache")
+    _cache_ok(v_cache, desc, "v_cache")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.pkv_append_decode(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q"),
+                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                _dev(block_tables, "block_tables", torch.int32),
+                                int(block_tables.shape[1]),
+                                _dev(context_lens, "context_lens", torch.int32), B, Hq,
+                                int(max_context_len), float(scale), _dev(out, "out"),
+                                _dtype_code(out), int(num_splits), _dev(workspace, "workspace"),
+                                ws_bytes, ctypes.byref(desc.c()), _stream(stream))
+    _check(rc, "pkv_append_decode")
 
 
 def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, max_query_len: int,

@@ -138,15 +138,18 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
     return ws_layout(num_seqs, num_q_heads, W, c->head_dim).total;
 }
 
-extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
-                          const int32_t *block_tables, int32_t block_table_stride,
-                          const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                          int32_t max_context_len, float scale, void *out, int32_t out_dtype,
-                          int32_t num_splits, void *workspace, size_t workspace_bytes,
-                          const pkv_cache_desc *c, void *stream)
+namespace {
+
+// Validation and launch shared by pkv_decode and pkv_append_decode (k_new
+// NULL for the plain decode).
+int decode_call(const char *who, const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_tables, int32_t block_table_stride,
+                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+                int32_t num_splits, void *workspace, size_t workspace_bytes,
+                const pkv_cache_desc *c, void *stream, const void *k_new, const void *v_new,
+                const int32_t *slots)
 {
-    static const char *who = "pkv_decode";
-    pkv::clear_error();
     int rc = check_desc(c, who);
     if (rc || (rc = check_heads(num_q_heads, c, who)))
         return rc;
@@ -173,6 +176,12 @@ extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cach
         return rc;
     if (!block_tables || !context_lens)
         return fail(PKV_EINVAL, "%s: block_tables or context_lens is NULL", who);
+    if (k_new || v_new || slots) {
+        if ((rc = check_ptr(k_new, "k_new", who)) || (rc = check_ptr(v_new, "v_new", who)))
+            return rc;
+        if (!slots)
+            return fail(PKV_EINVAL, "%s: slot_mapping is NULL", who);
+    }
     const int32_t W = num_splits > 0 ? num_splits : auto_splits(num_seqs, max_context_len, c);
     const WsLayout lay = ws_layout(num_seqs, num_q_heads, W, c->head_dim);
     if ((rc = check_ptr(workspace, "workspace", who)))
@@ -203,8 +212,47 @@ extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cach
     d.ws_pref = reinterpret_cast<int32_t *>(ws + lay.pref);
     d.ws_o = reinterpret_cast<float *>(ws + lay.o);
     d.ws_ml = reinterpret_cast<float *>(ws + lay.ml);
+    d.k_new = k_new;
+    d.v_new = v_new;
+    d.slots = slots;
+    d.k_cache_w = const_cast<void *>(k_cache);
+    d.v_cache_w = const_cast<void *>(v_cache);
     d.stream = stream;
     return pkv::launch_decode(d);
+}
+
+}  // namespace
+
+extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_tables, int32_t block_table_stride,
+                          const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+                          int32_t num_splits, void *workspace, size_t workspace_bytes,
+                          const pkv_cache_desc *c, void *stream)
+{
+    pkv::clear_error();
+    return decode_call("pkv_decode", q, k_cache, v_cache, block_tables, block_table_stride,
+                       context_lens, num_seqs, num_q_heads, max_context_len, scale, out, out_dtype,
+                       num_splits, workspace, workspace_bytes, c, stream, nullptr, nullptr,
+                       nullptr);
+}
+
+extern "C" int pkv_append_decode(const void *k_new, const void *v_new,
+                                 const int32_t *slot_mapping, const void *q, void *k_cache,
+                                 void *v_cache, const int32_t *block_tables,
+                                 int32_t block_table_stride, const int32_t *context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 float scale, void *out, int32_t out_dtype, int32_t num_splits,
+                                 void *workspace, size_t workspace_bytes, const pkv_cache_desc *c,
+                                 void *stream)
+{
+    pkv::clear_error();
+    if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+        return fail(PKV_EINVAL, "pkv_append_decode: k_new, v_new or slot_mapping is NULL");
+    return decode_call("pkv_append_decode", q, k_cache, v_cache, block_tables, block_table_stride,
+                       context_lens, num_seqs, num_q_heads, max_context_len, scale, out, out_dtype,
+                       num_splits, workspace, workspace_bytes, c, stream, k_new, v_new,
+                       slot_mapping);
 }
 
 extern "C" size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

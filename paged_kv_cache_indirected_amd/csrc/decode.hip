@@ -79,6 +79,13 @@ struct Args {
     float *ws_o;                      // [Hkv][W + B][G][D] partial outputs
     float *ws_ml;                     // [Hkv][W + B][G][2] running max (log2 units), sum
     int32_t *ws_pref;                 // [B + 1] block prefix sums, for the merge pass
+    const void *k_new;                // fused append: [B][Hkv][D] rows (NULL: none)
+    const void *v_new;
+    const int32_t *slots;             // fused append: slot of sequence b's new row
+    void *kc_w;                       // the caches, written by the fused append
+    void *vc_w;
+    int32_t row_chunks;               // 16-byte chunks per K/V row (LPT)
+    int32_t block_size;
     int32_t stride;
     int32_t B, Hq, Hkv, num_blocks;
     int32_t W;                        // workgroups per KV head
@@ -304,6 +311,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
 
     __shared__ int32_t lds_pref[kDecodeMaxSeqs + 1];
     __shared__ __attribute__((aligned(16))) uint4 lds_q[G * LPT];
+    __shared__ __attribute__((aligned(16))) uint4 lds_new[2][LPT];   // fused append: K, V row
     __shared__ int32_t lds_ids[kIdChunk];
     __shared__ int32_t lds_wsum[NW];
     __shared__ float lds_o[NW][G * D];
@@ -395,6 +403,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
             for (int i = tid; i < G * LPT; i += kThreads)
                 lds_q[i] = qp[i];
         }
+        // Fused append: the workgroup holding the sequence's last block
+        // writes the step's new K/V row of this KV head to its slot, and
+        // keeps it in LDS so that the attention reads position L-1 from it
+        // rather than from the cache written in the same launch.
+        const int nslot = (a.k_new && j1 == nblk) ? a.slots[b] : -1;
+        const bool fresh = (unsigned)nslot < (unsigned)(a.num_blocks * BS);
+        if (fresh && tid < 2 * LPT) {
+            const int kv = tid / LPT, i = tid % LPT;
+            const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
+                [((int64_t)b * a.Hkv + g) * LPT + i];
+            lds_new[kv][i] = row;
+            const int64_t dst = (((int64_t)(nslot / BS) * a.Hkv + g) * BS + nslot % BS) * LPT + i;
+            static_cast<uint4 *>(kv ? a.vc_w : a.kc_w)[dst] = row;
+        }
         __syncthreads();
 
         float o[G][CH];
@@ -437,9 +459,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
         };
 
         // One sub-tile: QK^T, online softmax update, PV.
-        auto process = [&](int e, int id, const uint4 (&kr)[TPR], uint4 (&vr)[TPR]) {
+        auto process = [&](int e, int id, uint4 (&kr)[TPR], uint4 (&vr)[TPR]) {
             const int j = blk_of(e);
             const bool ok = (unsigned)id < (unsigned)a.num_blocks;
+            if (fresh && j == nblk - 1) {
+                const int pl = j * BS + (e % NSUBT) * SUBTOK + r;   // position of token row 0
+#pragma unroll
+                for (int t = 0; t < TPR; ++t)
+                    if (pl + t * R == L - 1) {
+                        kr[t] = lds_new[0][li];
+                        vr[t] = lds_new[1][li];
+                    }
+            }
             float acc[G][TPR];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -673,6 +704,20 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
     const int64_t oidx = ((int64_t)b * a.Hq + hq) * D + d;
     if (se == sb) {
         store_out(a.out, a.out_dtype, oidx, 0.0f);
+        // Fused append of a sequence with no blocks: no split workgroup
+        // visits it, so its new row is written here.
+        if (a.k_new && h == 0 && d < 2 * a.row_chunks) {
+            const int nslot = a.slots[b];
+            const int bsz = a.stride > 0 ? a.block_size : 1;
+            if ((unsigned)nslot < (unsigned)(a.num_blocks * bsz)) {
+                const int kv = d / a.row_chunks, i = d % a.row_chunks;
+                const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
+                    [((int64_t)b * a.Hkv + g) * a.row_chunks + i];
+                const int64_t dst = (((int64_t)(nslot / bsz) * a.Hkv + g) * bsz + nslot % bsz) *
+                                        a.row_chunks + i;
+                static_cast<uint4 *>(kv ? a.vc_w : a.kc_w)[dst] = row;
+            }
+        }
         return;
     }
     const int wf = owner(sb, T, a.W), wl = owner(se - 1, T, a.W);
@@ -779,6 +824,17 @@ int launch_decode(const DecodeLaunch &d)
         a.ws_o = d.ws_o;
         a.ws_ml = d.ws_ml;
         a.ws_pref = d.ws_pref;
+        a.k_new = d.k_new ? static_cast<const char *>(d.k_new) +
+                                (int64_t)b0 * d.num_kv_heads * d.head_dim * esz
+                          : nullptr;
+        a.v_new = d.v_new ? static_cast<const char *>(d.v_new) +
+                                (int64_t)b0 * d.num_kv_heads * d.head_dim * esz
+                          : nullptr;
+        a.slots = d.slots ? d.slots + b0 : nullptr;
+        a.kc_w = d.k_cache_w;
+        a.vc_w = d.v_cache_w;
+        a.row_chunks = d.head_dim * esz / 16;
+        a.block_size = d.block_size;
         a.stride = d.table_stride;
         a.B = nb;
         a.Hq = d.num_q_heads;

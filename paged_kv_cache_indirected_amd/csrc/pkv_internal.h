@@ -41,6 +41,11 @@ struct DecodeLaunch {
     int32_t *ws_pref;          // [Bc + 1] block prefix sums
     float *ws_o;               // [Hkv][W + Bc][G][D] partial outputs
     float *ws_ml;              // [Hkv][W + Bc][G][2] running max (log2 units) and sum
+    const void *k_new;         // fused append (NULL: plain decode): [B][Hkv][D]
+    const void *v_new;
+    const int32_t *slots;      // [B]
+    void *k_cache_w;           // writable views of the caches for the fused append
+    void *v_cache_w;
     void *stream;
 };
 int launch_decode(const DecodeLaunch &a);

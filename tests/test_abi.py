@@ -141,3 +141,21 @@ def test_single_hip_runtime_in_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          cwd=ROOT, check=True).stdout.strip()
     assert out == "1"
+
+
+def test_append_decode_rejects():
+    d = _desc()
+    f = L.pkv_append_decode
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 64, 100, 0.1, FAKE, pkv.F32, 0,
+            FAKE, 1 << 30, ctypes.byref(d), None]
+    for i, code in ((0, pkv.EINVAL), (1, pkv.EINVAL), (2, pkv.EINVAL)):
+        bad = list(args)
+        bad[i] = None
+        assert f(*bad) == code
+    bad = list(args)
+    bad[0] = MIS
+    assert f(*bad) == pkv.EINVAL
+    bad = list(args)
+    bad[9] = 0      # empty batch: a no-op even without rows
+    bad[0] = bad[1] = bad[2] = None
+    assert f(*bad) == pkv.OK

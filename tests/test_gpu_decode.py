@@ -208,3 +208,104 @@ def test_workspace_reused_across_calls():
                        mx, workspace=ws, num_splits=ns)
             torch.cuda.synchronize()
             assert max_err(out, ref) <= TOL["bf16"], ns
+
+
+def _step_state(batch, pool_seed=None):
+    """Cache holding every row but each sequence's last; the step's slots
+    from the pool; the last rows as device tensors."""
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    from harness import DT
+    sh = batch.shape
+    st = batch.seq_start()
+    ids = list(range(batch.B))
+    cache = PagedCache(batch.pool_blocks, sh.Hkv, sh.block_size, sh.D, DT[sh.dtype],
+                       pool_seed=batch.pool_seed if pool_seed is None else pool_seed)
+    cache.add_sequences(ids, batch.lens - 1,
+                        np.concatenate([batch.k[st[b]:st[b + 1] - 1] for b in ids]),
+                        np.concatenate([batch.v[st[b]:st[b + 1] - 1] for b in ids]))
+    slots = cache.seqs.append_batch(ids)
+    tables, lens, mx = cache.tables(ids)
+    last = st[1:] - 1
+    return (cache, torch.from_numpy(slots).to("cuda"),
+            to_device_rows(batch.k[last], DT[sh.dtype], "cuda"),
+            to_device_rows(batch.v[last], DT[sh.dtype], "cuda"),
+            to_device_rows(batch.q, DT[sh.dtype], "cuda"), tables, lens, mx)
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "ragged-bs32-f32"])
+def test_append_decode_equals_append_then_decode_bitwise(name):
+    import paged_kv_cache_indirected_amd as pkv
+    if name == "cfg1":
+        b = synth.cfg1()
+    elif name == "cfg2":
+        b = synth.cfg2(B=8)
+    else:
+        b = synth.custom_decode(15, [1, 2, 31, 32, 33, 100], Hq=8, Hkv=2, D=128, dtype="f32",
+                                block_size=32)
+    say(f"[append_decode] {name}")
+    cache, slots, kn, vn, q, tab, lens, mx = _step_state(b)
+    kc0, vc0 = cache.k_cache.clone(), cache.v_cache.clone()
+    B, Hq, D = q.shape
+    for ns in (0, 3):
+        ws = torch.zeros(pkv.decode_workspace_bytes(B, Hq, mx, cache.desc, ns), dtype=torch.uint8,
+                         device="cuda")
+        cache.k_cache.copy_(kc0)
+        cache.v_cache.copy_(vc0)
+        o1 = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        pkv.append(kn, vn, slots, cache.k_cache, cache.v_cache, cache.desc)
+        pkv.decode(q, cache.k_cache, cache.v_cache, tab, lens, b.shape.scale, o1, cache.desc, mx,
+                   workspace=ws, num_splits=ns)
+        torch.cuda.synchronize()
+        k1, v1 = cache.k_cache.clone(), cache.v_cache.clone()
+        cache.k_cache.copy_(kc0)
+        cache.v_cache.copy_(vc0)
+        o2 = torch.empty_like(o1)
+        pkv.append_decode(kn, vn, slots, q, cache.k_cache, cache.v_cache, tab, lens, b.shape.scale,
+                          o2, cache.desc, mx, workspace=ws, num_splits=ns)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        assert torch.equal(k1.view(torch.uint8), cache.k_cache.view(torch.uint8))
+        assert torch.equal(v1.view(torch.uint8), cache.v_cache.view(torch.uint8))
+    ref = oracle.decode(b.q, b.k, b.v, b.lens, b.shape.scale)
+    assert max_err(o2, ref) <= TOL[b.shape.dtype]
+
+
+def test_append_decode_skipped_slots_and_empty_sequences():
+    # A negative slot appends nothing (position L-1 then comes from the
+    # cache, written beforehand here); a sequence of length 0 still gets its
+    # row written and a zero output.
+    import paged_kv_cache_indirected_amd as pkv
+    b = synth.custom_decode(16, [40, 1, 17, 300], Hq=16, Hkv=2, D=128, dtype="bf16",
+                            block_size=16)
+    cache, slots, kn, vn, q, tab, lens, mx = _step_state(b)
+    pkv.append(kn[:1], vn[:1], slots[:1], cache.k_cache, cache.v_cache, cache.desc)
+    slots_f = slots.clone()
+    slots_f[0] = -1
+    lens[2] = 0
+    torch.cuda.synchronize()
+    kc0, vc0 = cache.k_cache.clone(), cache.v_cache.clone()
+    B, Hq, D = q.shape
+    ws = torch.zeros(pkv.decode_workspace_bytes(B, Hq, mx, cache.desc, 0), dtype=torch.uint8,
+                     device="cuda")
+    o2 = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    pkv.append_decode(kn, vn, slots_f, q, cache.k_cache, cache.v_cache, tab, lens, b.shape.scale,
+                      o2, cache.desc, mx, workspace=ws)
+    torch.cuda.synchronize()
+    k2, v2 = cache.k_cache.clone(), cache.v_cache.clone()
+    cache.k_cache.copy_(kc0)
+    cache.v_cache.copy_(vc0)
+    o1 = torch.empty_like(o2)
+    pkv.append(kn, vn, slots_f, cache.k_cache, cache.v_cache, cache.desc)
+    pkv.decode(q, cache.k_cache, cache.v_cache, tab, lens, b.shape.scale, o1, cache.desc, mx,
+               workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(k2.view(torch.uint8), cache.k_cache.view(torch.uint8))
+    assert torch.equal(v2.view(torch.uint8), cache.v_cache.view(torch.uint8))
+    assert torch.count_nonzero(o2[2]) == 0
+    keep = [0, 1, 3]
+    st = b.seq_start()
+    ref = oracle.decode(b.q[keep], np.concatenate([b.k[st[i]:st[i + 1]] for i in keep]),
+                        np.concatenate([b.v[st[i]:st[i + 1]] for i in keep]), b.lens[keep],
+                        b.shape.scale)
+    assert max_err(o2[keep], ref) <= TOL["bf16"]
