@@ -66,6 +66,9 @@ def _load():
     lib.oracle_prefill.restype = i32
     lib.oracle_append.argtypes = [P, P, P, i32, i32, i32, i32, i32, ctypes.c_int64, P, P]
     lib.oracle_append.restype = i32
+    lib.oracle_copy_blocks.argtypes = [P, P, ctypes.c_int64, P, P, ctypes.c_int64, P, P, i32, i32,
+                                       i32, i32, i32]
+    lib.oracle_copy_blocks.restype = i32
     lib.oracle_kv_bytes_per_layer.argtypes = [ctypes.c_int64] * 4
     lib.oracle_kv_bytes_per_layer.restype = ctypes.c_int64
     _lib = lib
@@ -203,6 +206,55 @@ def append(k, v, slots, k_cache: np.ndarray, v_cache: np.ndarray, block_size: in
                            int(block_size), nb, _ptr(k_cache), _ptr(v_cache))
     if rc != 0:
         raise ValueError("oracle_append: slot out of range or bad arguments")
+
+
+def copy_blocks(src_k, src_v, dst_k: np.ndarray, dst_v: np.ndarray, src_ids, dst_ids) -> None:
+    """Block copy between host copies of two caches (may be the same arrays),
+    in place: block dst_ids[i] of dst receives block src_ids[i] of src, pairs
+    in order, a pair with an id outside its cache skipped.
+
+    Sequences with an identical prefix share its pages (the "LLM Inference
+    Engineering" summary, section 2); copying a shared block before a sharer
+    writes into it is the reading taken where the pages are silent.
+    """
+    lib = _load()
+    src_ids = _c(np.asarray(src_ids, dtype=np.int32))
+    dst_ids = _c(np.asarray(dst_ids, dtype=np.int32))
+    if src_ids.shape != dst_ids.shape:
+        raise ValueError("id lists differ in length")
+    for a in (src_k, src_v, dst_k, dst_v):
+        if not a.flags.c_contiguous or a.ndim != 4:
+            raise ValueError("caches must be contiguous [num_blocks][Hkv][bs][D]")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination blocks differ")
+    _, Hkv, bs, D = src_k.shape
+    rc = lib.oracle_copy_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k),
+                                _ptr(dst_v), dst_k.shape[0], _ptr(src_ids), _ptr(dst_ids),
+                                len(src_ids), Hkv, bs, D, src_k.dtype.itemsize)
+    if rc != 0:
+        raise ValueError("oracle_copy_blocks rejected its arguments")
+
+
+def reusable_prefix_tokens(prompt, cached_prompts, block_size: int) -> int:
+    """Tokens of ``prompt`` a prefix cache can serve from earlier prompts.
+
+    The "LLM Inference: KV Cache, Batching & Scheduling" page, section
+    "Prefix caching": a prefix's KV is computed once and later requests pay
+    only for the tokens after it.  Readings: KV is cached per whole block, a
+    block is reusable only if every token up to its end matches (its KV
+    depends on the whole prefix), and at least one prompt token is always
+    left to compute.  So the answer is the longest common prefix with any
+    earlier prompt, rounded down to whole blocks, capped at
+    (len(prompt) - 1) // block_size blocks.
+    """
+    best = 0
+    for c in cached_prompts:
+        k = 0
+        while k < min(len(prompt), len(c)) and prompt[k] == c[k]:
+            k += 1
+        best = max(best, k // block_size)
+    cap = (len(prompt) - 1) // block_size if len(prompt) > 0 else 0
+    return min(best, cap) * block_size
 
 
 def kv_bytes_per_layer(seq_len: int, num_kv_heads: int, head_dim: int, elem_size: int) -> int:

@@ -282,6 +282,37 @@ int oracle_append(const void *k, const void *v, const int32_t *slots, int T, int
 }
 
 /*
+ * Block copy (sharing of identical prefixes, [KV-news] section 2 and
+ * [KV-blog] "The Elegant Fix"; the copy made before a sharer writes into a
+ * shared block is this library's reading, the pages are silent on writes to
+ * shared pages).  For pair i, every (KV head, offset) row of block
+ * dst_ids[i] in each destination tensor becomes the same row of block
+ * src_ids[i] in the source tensor.  A pair naming a block outside its cache
+ * is skipped.  Pairs are applied in order.
+ */
+int oracle_copy_blocks(const void *src_k, const void *src_v, int64_t src_nb, void *dst_k,
+                       void *dst_v, int64_t dst_nb, const int32_t *src_ids,
+                       const int32_t *dst_ids, int n, int Hkv, int bs, int D, int elem_size)
+{
+    if (n < 0 || Hkv <= 0 || bs <= 0 || D <= 0 || (elem_size != 2 && elem_size != 4))
+        return -1;
+    const size_t row = (size_t)D * (size_t)elem_size;
+    for (int i = 0; i < n; ++i) {
+        const int64_t s = src_ids[i], d = dst_ids[i];
+        if (s < 0 || s >= src_nb || d < 0 || d >= dst_nb)
+            continue;
+        for (int g = 0; g < Hkv; ++g)
+            for (int o = 0; o < bs; ++o) {
+                size_t from = (((size_t)s * Hkv + g) * bs + o) * row;
+                size_t to = (((size_t)d * Hkv + g) * bs + o) * row;
+                memcpy((char *)dst_k + to, (const char *)src_k + from, row);
+                memcpy((char *)dst_v + to, (const char *)src_v + from, row);
+            }
+    }
+    return 0;
+}
+
+/*
  * Per-layer KV-cache bytes ([KV-prep] "The KV cache", memory-cost formula):
  * two tensors (K and V) x tokens x KV heads x head_dim x element size.
  */

@@ -312,6 +312,68 @@ def test_append_rejects_out_of_range_slot():
 # --------------------------------------------------------------------------
 # The page's worked sizing example.
 
+# --------------------------------------------------------------------------
+# Block copy: a hand-written image, logical read-back through the slot rule,
+# and the skip rule.
+
+def test_copy_blocks_tiny_image_by_hand():
+    # 3 blocks x 1 KV head x block 2 x D 2, float32; copy block 2 -> block 0.
+    kc = np.arange(12, dtype=np.float32).reshape(3, 1, 2, 2)
+    vc = -kc
+    oracle.copy_blocks(kc, vc, kc, vc, [2], [0])
+    exp = np.array([8, 9, 10, 11, 4, 5, 6, 7, 8, 9, 10, 11], dtype=np.float32).reshape(3, 1, 2, 2)
+    assert np.array_equal(kc, exp) and np.array_equal(vc, -exp)
+
+
+def test_copy_blocks_preserves_logical_rows_through_append():
+    # A sequence written by append through block list [a, b]; after copying
+    # a -> c and b -> d, reading the sequence through [c, d] gives the rows
+    # that were appended, in order, for every head.
+    g = np.random.default_rng(11)
+    nb, H, bs, D, T = 8, 3, 4, 5, 7
+    k = g.integers(0, 2**16, size=(T, H, D), dtype=np.uint16)
+    v = g.integers(0, 2**16, size=(T, H, D), dtype=np.uint16)
+    blocks = [5, 2]
+    slots = [blocks[t // bs] * bs + t % bs for t in range(T)]
+    kc = np.zeros((nb, H, bs, D), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    oracle.append(k, v, slots, kc, vc, bs)
+    dk, dv = np.zeros_like(kc), np.zeros_like(vc)
+    oracle.copy_blocks(kc, vc, dk, dv, blocks, [0, 7])
+    new = [0, 7]
+    for t in range(T):
+        assert np.array_equal(dk[new[t // bs], :, t % bs], k[t])
+        assert np.array_equal(dv[new[t // bs], :, t % bs], v[t])
+    untouched = [b for b in range(nb) if b not in new]
+    assert not dk[untouched].any() and not dv[untouched].any()
+
+
+def test_copy_blocks_skips_out_of_range_pairs():
+    kc = np.arange(2 * 2 * 2 * 4, dtype=np.float32).reshape(2, 2, 2, 4)
+    vc = kc + 100
+    dk, dv = np.full_like(kc, -1), np.full_like(vc, -1)
+    oracle.copy_blocks(kc, vc, dk, dv, [-1, 2, 0, 1], [0, 1, 2, 1])
+    assert np.all(dk[0] == -1)                      # src -1: skipped
+    assert np.array_equal(dk[1], kc[1]) and np.array_equal(dv[1], vc[1])   # only (1 -> 1)
+
+
+# --------------------------------------------------------------------------
+# Prefix cache: reusable tokens, worked by hand.
+
+@pytest.mark.parametrize("prompt,cached,bs,expect", [
+    ([1, 2, 3, 4, 5, 6, 7, 8, 9], [[1, 2, 3, 4, 5, 6, 7, 8]], 4, 8),
+    ([1, 2, 3, 4, 5, 6, 7, 8], [[1, 2, 3, 4, 5, 6, 7, 8]], 4, 4),    # one token left to compute
+    ([1, 2, 3, 4, 5, 6, 7, 0, 9], [[1, 2, 3, 4, 5, 6, 7, 8]], 4, 4),  # second block differs
+    ([0, 2, 3, 4, 5, 6, 7, 8, 9], [[1, 2, 3, 4, 5, 6, 7, 8]], 4, 0),  # first token differs
+    ([1, 2, 3, 4, 5, 6, 7, 8, 9], [[1, 2, 3], [1, 2, 3, 4, 5]], 4, 4),
+    ([], [[1, 2]], 2, 0),
+    ([7], [[7]], 1, 0),
+    ([7, 8], [[7, 8, 9]], 1, 1),
+])
+def test_reusable_prefix_tokens_by_hand(prompt, cached, bs, expect):
+    assert oracle.reusable_prefix_tokens(prompt, cached, bs) == expect
+
+
 def test_kv_sizing_worked_example():
     with open(os.path.join(GOLDEN, "kv_sizing.json")) as f:
         ex = json.load(f)
