@@ -85,6 +85,30 @@ int pkv_append(const void *k, const void *v, const int32_t *slot_mapping, int32_
                void *k_cache, void *v_cache, const pkv_cache_desc *c, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Block copy.  Sequences with an identical prefix share its pages ([KV-news]
+ * section 2, [KV-blog] "The Elegant Fix"); before one of them writes into a
+ * shared, partially filled block it needs a private copy (copy-on-write, this
+ * library's reading: the pages say nothing of writes to shared pages).  The
+ * same call moves blocks to or from a second cache of the same block shape,
+ * e.g. a swap area in pinned host memory.
+ *
+ *   src_k, src_v, src_c  source caches and their descriptor
+ *   dst_k, dst_v, dst_c  destination caches (may be the source caches); the
+ *                        descriptors must agree in num_kv_heads, block_size,
+ *                        head_dim and dtype
+ *   src_ids, dst_ids     [n] int32, device-readable: block dst_ids[i] of the
+ *                        destination receives block src_ids[i] of the source
+ *                        (K and V, every KV head and offset).  A pair with an
+ *                        id outside its cache is skipped.  Destination blocks
+ *                        must be distinct and, when the caches are the same,
+ *                        disjoint from the source blocks.
+ * Copies bits.  n == 0 is a no-op.
+ */
+int pkv_copy_blocks(const void *src_k, const void *src_v, const pkv_cache_desc *src_c,
+                    void *dst_k, void *dst_v, const pkv_cache_desc *dst_c,
+                    const int32_t *src_ids, const int32_t *dst_ids, int32_t n, void *stream);
+
+/* ------------------------------------------------------------------------
  * Paged decode attention ([KV-prep] "The KV cache": the query attends the
  * keys and values of every prior position; [KV-news] section 2 and
  * [KV-prep] "PagedAttention and vLLM": those positions live in fixed-size
@@ -202,12 +226,19 @@ int pkv_pool_alloc(pkv_pool *pool, int32_t n, int32_t *ids);
  * free or unknown; then nothing changes). */
 int pkv_pool_share(pkv_pool *pool, int32_t n, const int32_t *ids);
 /* Drop one reference from each of n blocks; a block reaching 0 returns to the
- * back of the free list.  PKV_ESTATE if any id is free or unknown, or appears
+ * back of the free list, or, if the prefix cache holds it, to the back of the
+ * cache's LRU list.  PKV_ESTATE if any id is free or unknown, or appears
  * more often than its refcount; then nothing changes. */
 int pkv_pool_release(pkv_pool *pool, int32_t n, const int32_t *ids);
+/* Blocks that can be handed out: the free list plus unreferenced blocks kept
+ * by the prefix cache (those are reused, least recently released first, only
+ * once the free list is empty). */
 int32_t pkv_pool_num_free(const pkv_pool *pool);
+/* Unreferenced blocks kept by the prefix cache. */
+int32_t pkv_pool_num_cached(const pkv_pool *pool);
 int32_t pkv_pool_num_blocks(const pkv_pool *pool);
-/* Refcount of a block (0 = free), or -1 for an id outside the pool. */
+/* Refcount of a block (0 = free or kept only by the prefix cache), or -1 for
+ * an id outside the pool. */
 int32_t pkv_pool_refcount(const pkv_pool *pool, int32_t id);
 
 /* ------------------------------------------------------------------------
@@ -243,6 +274,41 @@ int pkv_seqs_append(pkv_seqs *seqs, int64_t seq_id, int32_t n, int32_t *slots);
 /* One token for each of n sequences (a decode step); slots[i] for seq_ids[i].
  * All-or-nothing across the batch. */
 int pkv_seqs_append_batch(pkv_seqs *seqs, int32_t n, const int64_t *seq_ids, int32_t *slots);
+/* New sequence holding all of src_id's blocks, the partially filled last one
+ * included (parallel sampling, beam search): every block gains a reference.
+ * The first append of either sequence into the shared last block must go
+ * through pkv_seqs_append_cow. */
+int pkv_seqs_fork(pkv_seqs *seqs, int64_t seq_id, int64_t src_id);
+/* pkv_seqs_append / pkv_seqs_append_batch with copy-on-write: a sequence
+ * whose slot would land in a shared, partially filled last block first gets
+ * a fresh block in its place, and the pair (old, new) is written to
+ * copy_src[c], copy_dst[c] (room for 1 pair, resp. n pairs); *num_copies
+ * receives the count.  The caller copies those blocks (pkv_copy_blocks)
+ * before the new tokens are written.  In a batch, copies are decided in
+ * order: if every holder of a shared block is in the batch, the last one
+ * keeps the original.  Allocation is all-or-nothing (PKV_ENOBLOCKS). */
+int pkv_seqs_append_cow(pkv_seqs *seqs, int64_t seq_id, int32_t n, int32_t *slots,
+                        int32_t *copy_src, int32_t *copy_dst, int32_t *num_copies);
+int pkv_seqs_append_batch_cow(pkv_seqs *seqs, int32_t n, const int64_t *seq_ids, int32_t *slots,
+                              int32_t *copy_src, int32_t *copy_dst, int32_t *num_copies);
+
+/* Prefix cache ([KV-prep] "Prefix caching": a prefix shared by many requests
+ * is computed once and later requests pay only for the tokens after it).
+ * Full blocks are registered under a chained key of their token ids (the key
+ * of block j covers tokens [0, (j+1) * block_size)); a lookup compares the
+ * stored ids, so a hash collision never returns wrong data.
+ *
+ * pkv_seqs_add_cached: new sequence for a prompt of n token ids; it takes
+ * the longest run of registered blocks matching the prompt's leading whole
+ * blocks, at most (n - 1) / block_size of them so that at least one token is
+ * left to compute.  Returns the number of tokens reused (the new sequence's
+ * length, a multiple of block_size) or a negative code.
+ * pkv_seqs_cache: register the sequence's full blocks holding tokens[0, n)
+ * (n <= its length; a partial last block is not registered).  The caller
+ * states that those blocks hold the KV of exactly these token ids.  A block
+ * registered earlier under other contents is re-registered. */
+int32_t pkv_seqs_add_cached(pkv_seqs *seqs, int64_t seq_id, const int32_t *tokens, int32_t n);
+int pkv_seqs_cache(pkv_seqs *seqs, int64_t seq_id, const int32_t *tokens, int32_t n);
 /* Remove a sequence and drop its block references at once. */
 int pkv_seqs_release(pkv_seqs *seqs, int64_t seq_id);
 /* Length of a sequence, or -1 if unknown. */

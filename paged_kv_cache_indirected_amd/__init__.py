@@ -6,8 +6,9 @@ torch supplies device memory and streams.  There is no fallback: if the
 library is not built, importing this package fails.
 
 Calls mirror the C ABI names: ``append`` (pkv_append), ``decode``
-(pkv_decode), ``prefill_chunk`` (pkv_prefill_chunk), ``Pool`` (pkv_pool_*)
-and ``Seqs`` (pkv_seqs_*).
+(pkv_decode), ``append_decode`` (pkv_append_decode), ``prefill_chunk``
+(pkv_prefill_chunk), ``copy_blocks`` (pkv_copy_blocks), ``Pool``
+(pkv_pool_*) and ``Seqs`` (pkv_seqs_*).
 """
 from __future__ import annotations
 
@@ -64,6 +65,7 @@ _sig("pkv_strerror", ctypes.c_char_p, ctypes.c_int)
 _sig("pkv_last_error", ctypes.c_char_p)
 _sig("pkv_abi_version", ctypes.c_int)
 _sig("pkv_append", ctypes.c_int, _P, _P, _P, _i32, _P, _P, _DESC, _P)
+_sig("pkv_copy_blocks", ctypes.c_int, _P, _P, _DESC, _P, _P, _DESC, _P, _P, _i32, _P)
 _sig("pkv_decode_num_splits", _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, ctypes.c_float, _P,
@@ -79,6 +81,7 @@ _sig("pkv_pool_alloc", ctypes.c_int, _P, _i32, _P)
 _sig("pkv_pool_share", ctypes.c_int, _P, _i32, _P)
 _sig("pkv_pool_release", ctypes.c_int, _P, _i32, _P)
 _sig("pkv_pool_num_free", _i32, _P)
+_sig("pkv_pool_num_cached", _i32, _P)
 _sig("pkv_pool_num_blocks", _i32, _P)
 _sig("pkv_pool_refcount", _i32, _P, _i32)
 _sig("pkv_seqs_create", _P, _P, _i32)
@@ -87,6 +90,11 @@ _sig("pkv_seqs_add", ctypes.c_int, _P, _i64)
 _sig("pkv_seqs_add_shared", ctypes.c_int, _P, _i64, _i64, _i32)
 _sig("pkv_seqs_append", ctypes.c_int, _P, _i64, _i32, _P)
 _sig("pkv_seqs_append_batch", ctypes.c_int, _P, _i32, _P, _P)
+_sig("pkv_seqs_fork", ctypes.c_int, _P, _i64, _i64)
+_sig("pkv_seqs_append_cow", ctypes.c_int, _P, _i64, _i32, _P, _P, _P, _P)
+_sig("pkv_seqs_append_batch_cow", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _P)
+_sig("pkv_seqs_add_cached", _i32, _P, _i64, _P, _i32)
+_sig("pkv_seqs_cache", ctypes.c_int, _P, _i64, _P, _i32)
 _sig("pkv_seqs_release", ctypes.c_int, _P, _i64)
 _sig("pkv_seqs_len", _i32, _P, _i64)
 _sig("pkv_seqs_block_ids", _i32, _P, _i64, _i32, _P)
@@ -193,6 +201,26 @@ def append(k, v, slot_mapping, k_cache, v_cache, desc: CacheDesc, stream=None) -
                          T, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                          ctypes.byref(desc.c()), _stream(stream))
     _check(rc, "pkv_append")
+
+
+def copy_blocks(src_k, src_v, src_desc: CacheDesc, dst_k, dst_v, dst_desc: CacheDesc,
+                src_ids, dst_ids, stream=None) -> None:
+    """pkv_copy_blocks: block dst_ids[i] of (dst_k, dst_v) receives block
+    src_ids[i] of (src_k, src_v).  The caches may be GPU tensors or pinned
+    host tensors (device-accessible); the id lists are int32 GPU tensors."""
+    torch = _torch()
+    n = int(src_ids.numel())
+    _need(int(dst_ids.numel()) == n, "src_ids and dst_ids differ in length")
+    for t, d, name in ((src_k, src_desc, "src_k"), (src_v, src_desc, "src_v"),
+                       (dst_k, dst_desc, "dst_k"), (dst_v, dst_desc, "dst_v")):
+        _cache_ok(t, d, name)
+        _need(t.is_contiguous() and (t.is_cuda or t.is_pinned()),
+              f"{name} must be a contiguous GPU or pinned host tensor")
+    rc = _lib.pkv_copy_blocks(src_k.data_ptr(), src_v.data_ptr(), ctypes.byref(src_desc.c()),
+                              dst_k.data_ptr(), dst_v.data_ptr(), ctypes.byref(dst_desc.c()),
+                              _dev(src_ids, "src_ids", torch.int32),
+                              _dev(dst_ids, "dst_ids", torch.int32), n, _stream(stream))
+    _check(rc, "pkv_copy_blocks")
 
 
 def decode_num_splits(num_seqs: int, num_q_heads: int, max_context_len: int,
@@ -340,6 +368,10 @@ class Pool:
         return int(_lib.pkv_pool_num_free(self._h))
 
     @property
+    def num_cached(self) -> int:
+        return int(_lib.pkv_pool_num_cached(self._h))
+
+    @property
     def num_blocks(self) -> int:
         return int(_lib.pkv_pool_num_blocks(self._h))
 
@@ -388,6 +420,53 @@ class Seqs:
         _check(_lib.pkv_seqs_append_batch(self._h, len(ids), ids.ctypes.data, out.ctypes.data),
                "pkv_seqs_append_batch")
         return out[:len(ids)]
+
+    def fork(self, seq_id: int, src_id: int) -> None:
+        _check(_lib.pkv_seqs_fork(self._h, int(seq_id), int(src_id)), "pkv_seqs_fork")
+
+    def append_cow(self, seq_id: int, n: int):
+        """Extend by n tokens with copy-on-write; returns (slots, copies),
+        copies a list of (src_block, dst_block) pairs to copy first."""
+        import numpy as np
+        out = np.empty(max(int(n), 1), dtype=np.int32)
+        cs, cd, nc = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.pkv_seqs_append_cow(self._h, int(seq_id), int(n), out.ctypes.data,
+                                        ctypes.byref(cs), ctypes.byref(cd), ctypes.byref(nc)),
+               "pkv_seqs_append_cow")
+        return out[:n], [(cs.value, cd.value)] if nc.value else []
+
+    def append_batch_cow(self, seq_ids):
+        """One token for each listed sequence with copy-on-write; returns
+        (slots, copies)."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        out = np.empty(max(n, 1), dtype=np.int32)
+        cs = np.empty(max(n, 1), dtype=np.int32)
+        cd = np.empty(max(n, 1), dtype=np.int32)
+        nc = ctypes.c_int32()
+        _check(_lib.pkv_seqs_append_batch_cow(self._h, n, ids.ctypes.data, out.ctypes.data,
+                                              cs.ctypes.data, cd.ctypes.data, ctypes.byref(nc)),
+               "pkv_seqs_append_batch_cow")
+        return out[:n], list(zip(cs[:nc.value].tolist(), cd[:nc.value].tolist()))
+
+    def add_cached(self, seq_id: int, tokens) -> int:
+        """New sequence reusing the longest cached whole-block prefix of the
+        prompt ``tokens``; returns the number of tokens reused."""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        r = int(_lib.pkv_seqs_add_cached(self._h, int(seq_id), t.ctypes.data if len(t) else None,
+                                         len(t)))
+        if r < 0:
+            raise PkvError(r, "pkv_seqs_add_cached")
+        return r
+
+    def cache(self, seq_id: int, tokens) -> None:
+        """Register the sequence's full blocks as holding ``tokens``."""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(_lib.pkv_seqs_cache(self._h, int(seq_id), t.ctypes.data if len(t) else None,
+                                   len(t)), "pkv_seqs_cache")
 
     def release(self, seq_id: int) -> None:
         _check(_lib.pkv_seqs_release(self._h, int(seq_id)), "pkv_seqs_release")

@@ -118,6 +118,38 @@ extern "C" int pkv_append(const void *k, const void *v, const int32_t *slot_mapp
     return pkv::launch_append(a);
 }
 
+extern "C" int pkv_copy_blocks(const void *src_k, const void *src_v, const pkv_cache_desc *src_c,
+                               void *dst_k, void *dst_v, const pkv_cache_desc *dst_c,
+                               const int32_t *src_ids, const int32_t *dst_ids, int32_t n,
+                               void *stream)
+{
+    static const char *who = "pkv_copy_blocks";
+    pkv::clear_error();
+    int rc;
+    if ((rc = check_desc(src_c, who)) || (rc = check_desc(dst_c, who)))
+        return rc;
+    if (src_c->num_kv_heads != dst_c->num_kv_heads || src_c->block_size != dst_c->block_size ||
+        src_c->head_dim != dst_c->head_dim || src_c->dtype != dst_c->dtype)
+        return fail(PKV_EINVAL, "%s: source and destination blocks differ in shape or dtype", who);
+    if (n < 0)
+        return fail(PKV_EINVAL, "%s: n %d", who, n);
+    if (n == 0)
+        return PKV_OK;
+    if ((rc = check_ptr(src_k, "src_k", who)) || (rc = check_ptr(src_v, "src_v", who)) ||
+        (rc = check_ptr(dst_k, "dst_k", who)) || (rc = check_ptr(dst_v, "dst_v", who)))
+        return rc;
+    if (!src_ids || !dst_ids)
+        return fail(PKV_EINVAL, "%s: block id list is NULL", who);
+    const int64_t block_bytes = (int64_t)src_c->num_kv_heads * src_c->block_size *
+                                src_c->head_dim * elem_size(src_c->dtype);
+    if (block_bytes > INT32_MAX / 2)
+        return fail(PKV_EINVAL, "%s: block of %lld bytes is too large", who,
+                    (long long)block_bytes);
+    pkv::CopyLaunch a{src_k, src_v, src_c->num_blocks, dst_k, dst_v, dst_c->num_blocks,
+                      src_ids, dst_ids, n, block_bytes, stream};
+    return pkv::launch_copy_blocks(a);
+}
+
 extern "C" int32_t pkv_decode_num_splits(int32_t num_seqs, int32_t num_q_heads,
                                          int32_t max_context_len, const pkv_cache_desc *c)
 {

@@ -68,6 +68,21 @@ struct AppendLaunch {
 };
 int launch_append(const AppendLaunch &a);
 
+struct CopyLaunch {
+    const void *src_k;
+    const void *src_v;
+    int32_t src_num_blocks;
+    void *dst_k;
+    void *dst_v;
+    int32_t dst_num_blocks;
+    const int32_t *src_ids;
+    const int32_t *dst_ids;
+    int32_t n;
+    int64_t block_bytes;   // multiple of 16, < 2^31
+    void *stream;
+};
+int launch_copy_blocks(const CopyLaunch &a);
+
 struct PrefillLaunch {
     const void *q;
     const int32_t *query_start;

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cstring>
 #include <deque>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -19,10 +20,30 @@
 
 using pkv::fail;
 
+namespace {
+// A block registered in the prefix cache: the token ids it holds and the key
+// of the block before it in the sequence (the chain makes a block's key
+// depend on the whole prefix, not only on its own tokens).
+struct CachedBlock {
+    uint64_t key = 0;
+    uint64_t parent = 0;
+    std::vector<int32_t> tokens;
+};
+}  // namespace
+
 struct pkv_pool {
     int32_t num_blocks = 0;
-    std::vector<int32_t> ref;     // refcount per block, 0 = free
+    std::vector<int32_t> ref;     // refcount per block, 0 = free or cached-only
     std::deque<int32_t> free_q;   // front is handed out next; released blocks go to the back
+    // Prefix cache ("LLM Inference: KV Cache, Batching & Scheduling",
+    // "Prefix caching"): full blocks keyed by their token chain.  A cached
+    // block whose last reference goes away is kept, unreferenced, in an LRU
+    // list and only reused for other data when the free list runs dry.
+    std::unordered_map<uint64_t, int32_t> index;     // key -> block
+    std::vector<CachedBlock> cached;                 // per block (key 0 = not cached)
+    std::list<int32_t> lru;                          // front = least recently released
+    std::vector<std::list<int32_t>::iterator> lru_at;
+    std::vector<char> in_lru;
 };
 
 namespace {
@@ -53,6 +74,9 @@ extern "C" pkv_pool *pkv_pool_create(int32_t num_blocks, uint64_t seed)
     try {
         p->num_blocks = num_blocks;
         p->ref.assign(num_blocks, 0);
+        p->cached.resize(num_blocks);
+        p->lru_at.resize(num_blocks);
+        p->in_lru.assign(num_blocks, 0);
         std::vector<int32_t> order(num_blocks);
         for (int32_t i = 0; i < num_blocks; ++i)
             order[i] = i;
@@ -77,16 +101,46 @@ extern "C" pkv_pool *pkv_pool_create(int32_t num_blocks, uint64_t seed)
 
 extern "C" void pkv_pool_destroy(pkv_pool *pool) { delete pool; }
 
+namespace {
+
+void forget(pkv_pool *p, int32_t id)
+{
+    CachedBlock &c = p->cached[id];
+    if (c.key != 0) {
+        auto it = p->index.find(c.key);
+        if (it != p->index.end() && it->second == id)
+            p->index.erase(it);
+        c = CachedBlock{};
+    }
+}
+
+void lru_remove(pkv_pool *p, int32_t id)
+{
+    if (p->in_lru[id]) {
+        p->lru.erase(p->lru_at[id]);
+        p->in_lru[id] = 0;
+    }
+}
+
+}  // namespace
+
 extern "C" int pkv_pool_alloc(pkv_pool *p, int32_t n, int32_t *ids)
 {
     if (!p || n < 0 || (n > 0 && !ids))
         return fail(PKV_EINVAL, "pkv_pool_alloc: bad arguments");
-    if ((size_t)n > p->free_q.size())
+    if ((size_t)n > p->free_q.size() + p->lru.size())
         return fail(PKV_ENOBLOCKS, "pkv_pool_alloc: %d blocks requested, %zu free", n,
-                    p->free_q.size());
+                    p->free_q.size() + p->lru.size());
     for (int32_t i = 0; i < n; ++i) {
-        int32_t id = p->free_q.front();
-        p->free_q.pop_front();
+        int32_t id;
+        if (!p->free_q.empty()) {
+            id = p->free_q.front();
+            p->free_q.pop_front();
+        } else {   // evict the least recently released cached block
+            id = p->lru.front();
+            lru_remove(p, id);
+            forget(p, id);
+        }
         p->ref[id] = 1;
         ids[i] = id;
     }
@@ -118,12 +172,109 @@ extern "C" int pkv_pool_release(pkv_pool *p, int32_t n, const int32_t *ids)
                         ids[i]);
     }
     for (int32_t i = 0; i < n; ++i)
-        if (--p->ref[ids[i]] == 0)
-            p->free_q.push_back(ids[i]);
+        if (--p->ref[ids[i]] == 0) {
+            const int32_t id = ids[i];
+            if (p->cached[id].key != 0) {
+                p->lru_at[id] = p->lru.insert(p->lru.end(), id);
+                p->in_lru[id] = 1;
+            } else {
+                p->free_q.push_back(id);
+            }
+        }
     return PKV_OK;
 }
 
-extern "C" int32_t pkv_pool_num_free(const pkv_pool *p) { return p ? (int32_t)p->free_q.size() : -1; }
+extern "C" int32_t pkv_pool_num_free(const pkv_pool *p)
+{
+    return p ? (int32_t)(p->free_q.size() + p->lru.size()) : -1;
+}
+
+extern "C" int32_t pkv_pool_num_cached(const pkv_pool *p)
+{
+    return p ? (int32_t)p->lru.size() : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Prefix cache.
+
+namespace {
+
+constexpr uint64_t kChainSeed = 0x243F6A8885A308D3ull;   // key "before" the first block
+
+// Key of a block from its parent's key and its token ids: 64-bit FNV-1a over
+// the parent key's and the tokens' bytes, forced non-zero (0 marks "not
+// cached").  Collisions are caught on lookup by comparing the stored tokens
+// and parent key.
+uint64_t block_key(uint64_t parent, const int32_t *toks, int32_t bs)
+{
+    uint64_t h = 0xCBF29CE484222325ull;
+    auto mix = [&](uint64_t v, int nbytes) {
+        for (int i = 0; i < nbytes; ++i) {
+            h ^= (v >> (8 * i)) & 0xFF;
+            h *= 0x100000001B3ull;
+        }
+    };
+    mix(parent, 8);
+    for (int32_t i = 0; i < bs; ++i)
+        mix((uint32_t)toks[i], 4);
+    return h ? h : 1;
+}
+
+bool holds(const pkv_pool *p, int32_t id, uint64_t parent, const int32_t *toks, int32_t bs)
+{
+    const CachedBlock &c = p->cached[id];
+    return c.parent == parent && (int32_t)c.tokens.size() == bs &&
+           std::equal(c.tokens.begin(), c.tokens.end(), toks);
+}
+
+// Longest run of cached blocks holding tokens[0 .. k*bs), k <= cap; each
+// found block gains a reference (and leaves the LRU list).  Returns k.
+int32_t prefix_match(pkv_pool *p, int32_t block_size, const int32_t *tokens, int32_t n,
+                     int32_t *ids, int32_t cap)
+{
+    int32_t k = 0;
+    uint64_t parent = kChainSeed;
+    for (; k < cap && (int64_t)(k + 1) * block_size <= n; ++k) {
+        const int32_t *t = tokens + (int64_t)k * block_size;
+        const uint64_t key = block_key(parent, t, block_size);
+        auto it = p->index.find(key);
+        if (it == p->index.end() || !holds(p, it->second, parent, t, block_size))
+            break;
+        ids[k] = it->second;
+        parent = key;
+    }
+    for (int32_t i = 0; i < k; ++i) {
+        lru_remove(p, ids[i]);
+        ++p->ref[ids[i]];
+    }
+    return k;
+}
+
+// Register blocks ids[0 .. n/bs) (allocated) as holding tokens[0 .. n/bs*bs).
+void prefix_insert(pkv_pool *p, int32_t block_size, const int32_t *tokens, int32_t n,
+                   const int32_t *ids)
+{
+    const int32_t nb = n / block_size;
+    uint64_t parent = kChainSeed;
+    for (int32_t i = 0; i < nb; ++i) {
+        const int32_t *t = tokens + (int64_t)i * block_size;
+        const uint64_t key = block_key(parent, t, block_size);
+        auto it = p->index.find(key);
+        if (it == p->index.end()) {
+            // A block can hold one cached identity; re-registering it under
+            // another chain replaces the old entry.
+            forget(p, ids[i]);
+            p->index.emplace(key, ids[i]);
+            CachedBlock &c = p->cached[ids[i]];
+            c.key = key;
+            c.parent = parent;
+            c.tokens.assign(t, t + block_size);
+        }
+        parent = key;
+    }
+}
+
+}  // namespace
 
 extern "C" int32_t pkv_pool_num_blocks(const pkv_pool *p) { return p ? p->num_blocks : -1; }
 
@@ -195,6 +346,55 @@ extern "C" int pkv_seqs_add_shared(pkv_seqs *s, int64_t id, int64_t src, int32_t
     if (rc != PKV_OK)
         return rc;
     s->seqs.emplace(id, std::move(n));
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_fork(pkv_seqs *s, int64_t id, int64_t src)
+{
+    if (!s)
+        return fail(PKV_EINVAL, "pkv_seqs_fork: null handle");
+    auto it = s->seqs.find(src);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_fork: unknown source %lld", (long long)src);
+    if (s->seqs.count(id))
+        return fail(PKV_ESTATE, "pkv_seqs_fork: sequence %lld exists", (long long)id);
+    Seq n = it->second;
+    int rc = pkv_pool_share(s->pool, (int32_t)n.blocks.size(), n.blocks.data());
+    if (rc != PKV_OK)
+        return rc;
+    s->seqs.emplace(id, std::move(n));
+    return PKV_OK;
+}
+
+extern "C" int32_t pkv_seqs_add_cached(pkv_seqs *s, int64_t id, const int32_t *tokens, int32_t n)
+{
+    if (!s || n < 0 || (n > 0 && !tokens))
+        return fail(PKV_EINVAL, "pkv_seqs_add_cached: bad arguments");
+    if (s->seqs.count(id))
+        return fail(PKV_ESTATE, "pkv_seqs_add_cached: sequence %lld exists", (long long)id);
+    // At least one token is left to compute, so the prompt's last position
+    // always gets a fresh query.
+    const int32_t cap = n > 0 ? (n - 1) / s->bs : 0;
+    Seq q;
+    q.blocks.resize(cap);
+    const int32_t k = prefix_match(s->pool, s->bs, tokens, n, q.blocks.data(), cap);
+    q.blocks.resize(k);
+    q.len = k * s->bs;
+    s->seqs.emplace(id, std::move(q));
+    return k * s->bs;
+}
+
+extern "C" int pkv_seqs_cache(pkv_seqs *s, int64_t id, const int32_t *tokens, int32_t n)
+{
+    if (!s || n < 0 || (n > 0 && !tokens))
+        return fail(PKV_EINVAL, "pkv_seqs_cache: bad arguments");
+    auto it = s->seqs.find(id);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_cache: unknown sequence %lld", (long long)id);
+    if (n > it->second.len)
+        return fail(PKV_EINVAL, "pkv_seqs_cache: %d tokens given for a %d-token sequence", n,
+                    it->second.len);
+    prefix_insert(s->pool, s->bs, tokens, n, it->second.blocks.data());
     return PKV_OK;
 }
 
@@ -282,6 +482,94 @@ extern "C" int pkv_seqs_append_batch(pkv_seqs *s, int32_t n, const int64_t *ids,
             qs[i]->blocks.push_back(fresh[k++]);
         take_slots(s, *qs[i], 1, slots + i);
     }
+    return PKV_OK;
+}
+
+namespace {
+
+// Give sequence q a private copy of its shared, partially filled last block:
+// `fresh` replaces it in q's list and q's reference to the old block drops
+// (the old block stays allocated: other sequences still hold it).
+void cow_last(pkv_seqs *s, Seq &q, int32_t fresh, int32_t *src, int32_t *dst)
+{
+    const int32_t old = q.blocks.back();
+    q.blocks.back() = fresh;
+    pkv_pool_release(s->pool, 1, &old);
+    *src = old;
+    *dst = fresh;
+}
+
+}  // namespace
+
+extern "C" int pkv_seqs_append_cow(pkv_seqs *s, int64_t id, int32_t n, int32_t *slots,
+                                   int32_t *copy_src, int32_t *copy_dst, int32_t *num_copies)
+{
+    if (!s || n < 0 || (n > 0 && !slots) || !copy_src || !copy_dst || !num_copies)
+        return fail(PKV_EINVAL, "pkv_seqs_append_cow: bad arguments");
+    auto it = s->seqs.find(id);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_append_cow: unknown sequence %lld", (long long)id);
+    Seq &q = it->second;
+    if ((int64_t)q.len + n > INT32_MAX / 2)
+        return fail(PKV_EINVAL, "pkv_seqs_append_cow: sequence too long");
+    const bool cow = writes_shared_block(s, q, n);
+    const int32_t nb = blocks_needed(q, s->bs, n);
+    std::vector<int32_t> fresh(nb + (cow ? 1 : 0));
+    int rc = pkv_pool_alloc(s->pool, (int32_t)fresh.size(), fresh.data());
+    if (rc != PKV_OK)
+        return rc;
+    *num_copies = 0;
+    if (cow) {
+        cow_last(s, q, fresh.back(), copy_src, copy_dst);
+        *num_copies = 1;
+    }
+    q.blocks.insert(q.blocks.end(), fresh.begin(), fresh.begin() + nb);
+    take_slots(s, q, n, slots);
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_append_batch_cow(pkv_seqs *s, int32_t n, const int64_t *ids, int32_t *slots,
+                                         int32_t *copy_src, int32_t *copy_dst,
+                                         int32_t *num_copies)
+{
+    if (!s || n < 0 || (n > 0 && (!ids || !slots || !copy_src || !copy_dst)) || !num_copies)
+        return fail(PKV_EINVAL, "pkv_seqs_append_batch_cow: bad arguments");
+    std::vector<Seq *> qs(n);
+    std::unordered_map<int32_t, int32_t> sharers;   // shared partial last block -> batch sharers
+    int32_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = s->seqs.find(ids[i]);
+        if (it == s->seqs.end())
+            return fail(PKV_ESTATE, "pkv_seqs_append_batch_cow: unknown sequence %lld",
+                        (long long)ids[i]);
+        for (int32_t j = 0; j < i; ++j)
+            if (ids[j] == ids[i])
+                return fail(PKV_EINVAL, "pkv_seqs_append_batch_cow: sequence %lld listed twice",
+                            (long long)ids[i]);
+        qs[i] = &it->second;
+        if (writes_shared_block(s, *qs[i], 1))
+            ++sharers[qs[i]->blocks.back()];
+        total += blocks_needed(*qs[i], s->bs, 1);
+    }
+    // Copies are decided in batch order.  When every holder of a shared block
+    // is in the batch, the last of them to reach it keeps the original.
+    for (const auto &kv : sharers)
+        total += kv.second - (pkv_pool_refcount(s->pool, kv.first) == kv.second ? 1 : 0);
+    std::vector<int32_t> fresh(total);
+    int rc = pkv_pool_alloc(s->pool, total, fresh.data());
+    if (rc != PKV_OK)
+        return rc;
+    int32_t k = 0, c = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (writes_shared_block(s, *qs[i], 1)) {
+            cow_last(s, *qs[i], fresh[k++], copy_src + c, copy_dst + c);
+            ++c;
+        }
+        if (blocks_needed(*qs[i], s->bs, 1))
+            qs[i]->blocks.push_back(fresh[k++]);
+        take_slots(s, *qs[i], 1, slots + i);
+    }
+    *num_copies = c;
     return PKV_OK;
 }
 

@@ -4,9 +4,11 @@
 pool and the sequence bookkeeping, and loads K/V rows into the cache with
 ``pkv_append`` at the slots the pool hands out.  It is the host side of a
 serving step ("LLM Inference: KV Cache, Batching & Scheduling", sections
-"PagedAttention and vLLM" and "Continuous batching (Orca)"): sequences are
-added, grow by appends, share whole prefix blocks, and are released, their
-blocks returning to the pool at once.
+"PagedAttention and vLLM", "Continuous batching (Orca)" and "Prefix
+caching"): sequences are added, grow by appends, share prefix blocks (by
+explicit sharing, by forking, or through the prefix cache), and are
+released, their blocks returning to the pool at once.  A write into a
+shared, partially filled block first copies it (pkv_copy_blocks).
 """
 from __future__ import annotations
 
@@ -15,7 +17,7 @@ from typing import Iterable, Optional
 import numpy as np
 import torch
 
-from . import BF16, F32, CacheDesc, Pool, Seqs, append
+from . import BF16, F32, CacheDesc, Pool, Seqs, append, copy_blocks
 
 # Quiet-NaN bit patterns written into every cache element before any append,
 # so a read of an unused slot or block would surface in the output.
@@ -91,6 +93,41 @@ class PagedCache:
         slots = self.seqs.append(int(seq_id), len(k_rows))
         self.write(slots, k_rows, v_rows)
         return slots
+
+    def copy(self, copies) -> None:
+        """pkv_copy_blocks for a list of (src_block, dst_block) pairs."""
+        if not copies:
+            return
+        ids = torch.tensor(np.asarray(copies, dtype=np.int32).T.copy(), device=self.device)
+        copy_blocks(self.k_cache, self.v_cache, self.desc, self.k_cache, self.v_cache, self.desc,
+                    ids[0].contiguous(), ids[1].contiguous())
+
+    def fork(self, seq_id: int, src_id: int) -> None:
+        self.seqs.fork(int(seq_id), int(src_id))
+
+    def extend_cow(self, seq_id: int, k_rows: np.ndarray, v_rows: np.ndarray) -> np.ndarray:
+        """Append rows with copy-on-write of a shared partial last block."""
+        slots, copies = self.seqs.append_cow(int(seq_id), len(k_rows))
+        self.copy(copies)
+        self.write(slots, k_rows, v_rows)
+        return slots
+
+    def step_cow(self, seq_ids, k_rows: np.ndarray, v_rows: np.ndarray):
+        """One token for each sequence (a decode step) with copy-on-write.
+        Returns (slots, copies)."""
+        slots, copies = self.seqs.append_batch_cow(list(seq_ids))
+        self.copy(copies)
+        self.write(slots, k_rows, v_rows)
+        return slots, copies
+
+    def admit_cached(self, seq_id: int, tokens) -> int:
+        """New sequence for a prompt, reusing cached prefix blocks; returns
+        the number of prompt tokens whose KV is already in the cache."""
+        return self.seqs.add_cached(int(seq_id), tokens)
+
+    def register(self, seq_id: int, tokens) -> None:
+        """Record in the prefix cache that the sequence holds these tokens."""
+        self.seqs.cache(int(seq_id), tokens)
 
     def release(self, seq_id: int) -> None:
         self.seqs.release(int(seq_id))

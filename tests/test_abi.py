@@ -159,3 +159,21 @@ def test_append_decode_rejects():
     bad[9] = 0      # empty batch: a no-op even without rows
     bad[0] = bad[1] = bad[2] = None
     assert f(*bad) == pkv.OK
+
+
+def test_copy_blocks_rejects():
+    d = _desc()
+    f = L.pkv_copy_blocks
+
+    def call(sk=FAKE, sv=FAKE, sd=d, dk=FAKE, dv=FAKE, dd=d, si=FAKE, di=FAKE, n=4):
+        return f(sk, sv, ctypes.byref(sd), dk, dv, ctypes.byref(dd), si, di, n, None)
+    assert call(sk=None) == pkv.EINVAL
+    assert call(dv=MIS) == pkv.EINVAL
+    assert call(si=None) == pkv.EINVAL
+    assert call(n=-1) == pkv.EINVAL
+    assert call(dd=_desc(block_size=32)) == pkv.EINVAL          # block shapes differ
+    assert call(dd=_desc(dtype=pkv.F32)) == pkv.EINVAL
+    assert call(sd=_desc(head_dim=96)) == pkv.EUNSUPPORTED
+    assert call(n=0, sk=None, si=None) == pkv.OK                 # empty list: no-op
+    # Only the block shape must agree: the caches may differ in size.
+    assert call(n=0, dd=_desc(num_blocks=3)) == pkv.OK
