@@ -344,6 +344,113 @@ def bench_cfg5(timer, splits):
                          "one stream"}
 
 
+def bench_block_copy(timer):
+    """pkv_copy_blocks: copy-on-write style copies inside one cache, and a
+    sequence's blocks swapped out to pinned host memory and back."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    Hkv, bs, D = 8, 16, 128
+    nb = 16384                                   # 512 MiB per tensor
+    desc = pkv.CacheDesc(nb, Hkv, bs, D, pkv.BF16)
+    kc = torch.zeros(desc.cache_shape(), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    g = np.random.default_rng(17)
+    perm = g.permutation(nb)
+    n = 4096
+    src = torch.tensor(perm[:n].astype(np.int32), device="cuda")
+    dst = torch.tensor(perm[n:2 * n].astype(np.int32), device="cuda")
+    blk = Hkv * bs * D * 2 * 2                   # K + V bytes of one block
+    t = float(np.median(timer.per_call(
+        lambda: pkv.copy_blocks(kc, vc, desc, kc, vc, desc, src, dst), 20)))
+    res = {"workload": f"pkv_copy_blocks: {n} random block pairs in one cache of {nb} "
+                       "blocks (8 KV heads x 16 x 128 bf16)",
+           "ms_per_call": round(1e3 * t, 4),
+           "hbm_GBps_read_plus_write": round(2 * n * blk / t / 1e9, 1),
+           "frac_of_hbm_peak": round(2 * n * blk / t / 1e9 / HBM_PEAK_GBS, 4)}
+    # Swap: one 8192-token sequence (512 blocks) out to pinned host and back.
+    ns = 512
+    hdesc = pkv.CacheDesc(ns, Hkv, bs, D, pkv.BF16)
+    hk = torch.zeros(hdesc.cache_shape(), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    sids = torch.tensor(perm[:ns].astype(np.int32), device="cuda")
+    hids = torch.arange(ns, dtype=torch.int32, device="cuda")
+    t_out = float(np.median(timer.per_call(
+        lambda: pkv.copy_blocks(kc, vc, desc, hk, hv, hdesc, sids, hids), 10)))
+    t_in = float(np.median(timer.per_call(
+        lambda: pkv.copy_blocks(hk, hv, hdesc, kc, vc, desc, hids, sids), 10)))
+    res["swap"] = {"blocks": ns, "bytes": ns * blk,
+                   "out_ms": round(1e3 * t_out, 4), "out_GBps": round(ns * blk / t_out / 1e9, 1),
+                   "in_ms": round(1e3 * t_in, 4), "in_GBps": round(ns * blk / t_in / 1e9, 1),
+                   "note": "kernel reads/writes pinned host memory directly over PCIe"}
+    return res
+
+
+def bench_prefix_ttft(timer):
+    """TTFT proxy for prefix caching: the attention work of admitting one
+    2560-token prompt (2048 shared + 512 own) in 512-token prefill chunks,
+    cold (every chunk computed) vs with the 2048-token prefix served from
+    the prefix cache (one chunk).  Appends of the computed chunks included."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    import synth
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    Hq, Hkv, D, bs, C, P = 64, 8, 128, 16, 512, 2048
+    scale = 1.0 / np.sqrt(D)
+    total = P + C
+    g = synth.rng(46, synth.S_LENS)
+    tok_shared = g.integers(0, 32000, size=P)
+    tok_a = np.concatenate([tok_shared, g.integers(0, 32000, size=C)])
+    tok_b = np.concatenate([tok_shared, g.integers(0, 32000, size=C)])
+    k = synth.normal(synth.rng(46, synth.S_K), (total, Hkv, D), "bf16")
+    v = synth.normal(synth.rng(46, synth.S_V), (total, Hkv, D), "bf16")
+    q = synth.normal(synth.rng(46, synth.S_Q), (C, Hq, D), "bf16")
+    cache = PagedCache(1024, Hkv, bs, D, pkv.BF16, pool_seed=4601)
+    # Request A arrives cold and is registered; B shares its 2048-token prefix.
+    cache.admit_cached(0, tok_a)
+    cache.extend(0, k, v)
+    cache.register(0, tok_a)
+    reused = cache.admit_cached(1, tok_b)
+    cache.extend(1, k[reused:], v[reused:])
+    dq = to_device_rows(q, pkv.BF16, "cuda")
+    qs = torch.tensor([0, C], dtype=torch.int32, device="cuda")
+    out = torch.empty((C, Hq, D), dtype=torch.float32, device="cuda")
+    dk = to_device_rows(k, pkv.BF16, "cuda")
+    dv = to_device_rows(v, pkv.BF16, "cuda")
+    slots_a = torch.tensor(np.concatenate([
+        [b * bs + o for o in range(bs)] for b in cache.seqs.block_ids(0)])[:total].astype(
+            np.int32), device="cuda")
+    tab_a, _, _ = cache.tables([0])
+    tab_b, lens_b, mx_b = cache.tables([1])
+    lens_chunks = [torch.tensor([C * (i + 1)], dtype=torch.int32, device="cuda")
+                   for i in range(total // C)]
+    bb = cache.seqs.block_ids(1)
+    slots_b = torch.tensor(np.array([bb[p // bs] * bs + p % bs for p in range(reused, total)],
+                                    dtype=np.int32), device="cuda")
+
+    def cold():
+        for i in range(total // C):
+            lo = i * C
+            pkv.append(dk[lo:lo + C], dv[lo:lo + C], slots_a[lo:lo + C], cache.k_cache,
+                       cache.v_cache, cache.desc)
+            pkv.prefill_chunk(dq, qs, cache.k_cache, cache.v_cache, tab_a, lens_chunks[i],
+                              scale, out, cache.desc, C, C * (i + 1))
+
+    def warm():
+        pkv.append(dk[reused:], dv[reused:], slots_b, cache.k_cache, cache.v_cache, cache.desc)
+        pkv.prefill_chunk(dq, qs, cache.k_cache, cache.v_cache, tab_b, lens_b, scale, out,
+                          cache.desc, C, mx_b)
+    t_cold = float(np.median(timer.per_call(cold, 10)))
+    t_warm = float(np.median(timer.per_call(warm, 10)))
+    return {"workload": "prefix cache TTFT proxy: one 2560-token prompt (2048-token shared "
+                        "system prompt + 512 own), 512-token chunks, 64q/8kv, d128, bf16",
+            "tokens_reused": int(reused),
+            "cold_ms": round(1e3 * t_cold, 4),
+            "cached_ms": round(1e3 * t_warm, 4),
+            "ttft_reduction": round(1.0 - t_warm / t_cold, 4),
+            "note": "attention + KV append only (no model layers); the page's ~50% TTFT "
+                    "figure is for a whole model"}
+
+
 def probe_copy(nbytes=1 << 30, reps=3):
     """Run only the plain copy probe (nbytes read + nbytes written per call),
     so that a hardware-counter run sees a kernel of known traffic."""
@@ -414,6 +521,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads and the probes")
+    ap.add_argument("--only", choices=["continuous_batching", "prefix_sharing",
+                                       "chunked_prefill_mixed", "block_copy",
+                                       "prefix_cache_ttft"],
+                    help="run one secondary workload alone (for profiling) and print its JSON")
     ap.add_argument("--probe-copy", action="store_true",
                     help="run only the copy probe (for hardware-counter scaling)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -440,6 +551,14 @@ def main():
 
     torch.cuda.set_device(0)
     timer = Timer()
+    if args.only:
+        fns = {"continuous_batching": lambda: bench_cfg3(timer, 10, args.splits),
+               "prefix_sharing": lambda: bench_cfg4(timer, args.splits),
+               "chunked_prefill_mixed": lambda: bench_cfg5(timer, args.splits),
+               "block_copy": lambda: bench_block_copy(timer),
+               "prefix_cache_ttft": lambda: bench_prefix_ttft(timer)}
+        print(json.dumps({args.only: fns[args.only]()}), flush=True)
+        return
     batch = synth.cfg2()
     sh = batch.shape
     log(f"[bench] building {args.copies} paged copies of the Llama-70B-shaped batch "
@@ -563,6 +682,12 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] chunked prefill + decode")
         wl["chunked_prefill_mixed"] = bench_cfg5(timer, args.splits)
+        torch.cuda.empty_cache()
+        log("[bench] block copy and swap")
+        wl["block_copy"] = bench_block_copy(timer)
+        torch.cuda.empty_cache()
+        log("[bench] prefix cache TTFT proxy")
+        wl["prefix_cache_ttft"] = bench_prefix_ttft(timer)
         res["workloads"] = wl
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
