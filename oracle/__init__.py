@@ -192,8 +192,11 @@ def append(k, v, slots, k_cache: np.ndarray, v_cache: np.ndarray, block_size: in
 
     Follows the "LLM Inference: KV Cache, Batching & Scheduling" page, section
     "The KV cache" (the new token's K and V are appended each step).  Caches
-    are [num_blocks][Hkv][block_size][D]; slot s -> block s // block_size,
-    offset s % block_size; negative slots are skipped.
+    are [num_blocks][Hkv] tiles of block_size x D elements; slot s -> block
+    s // block_size, offset s % block_size; negative slots are skipped.
+    Inside a tile (the layout is a reading: the pages fix none) K element
+    (t, d) sits at ((d // E) * bs + t) * E + d % E, E = 16 // element size,
+    and V element (t, d) at ((t // 4) * D + d) * 4 + t % 4.
     """
     lib = _load()
     k, v = _c(k), _c(v)
@@ -206,6 +209,13 @@ def append(k, v, slots, k_cache: np.ndarray, v_cache: np.ndarray, block_size: in
                            int(block_size), nb, _ptr(k_cache), _ptr(v_cache))
     if rc != 0:
         raise ValueError("oracle_append: slot out of range or bad arguments")
+
+
+def tile_index(t: int, d: int, block_size: int, head_dim: int, elem_size: int):
+    """(K index, V index) of element (token offset t, dim d) inside one
+    (block, head) tile, in elements -- the layout ``append`` writes."""
+    E = 16 // elem_size
+    return ((d // E) * block_size + t) * E + d % E, ((t // 4) * head_dim + d) * 4 + t % 4
 
 
 def copy_blocks(src_k, src_v, dst_k: np.ndarray, dst_v: np.ndarray, src_ids, dst_ids) -> None:

@@ -28,9 +28,13 @@
  *   - an empty context gives a zero output row;
  *   - prefill row i of a chunk of C rows whose sequence holds L keys (the chunk
  *     already appended) attends keys [0, L - C + i], diagonal included;
- *   - the cache holds, per tensor, [num_blocks][num_kv_heads][block_size]
- *     [head_dim] elements, and slot s names block s / block_size, offset
- *     s % block_size; a negative slot is padding and writes nothing.
+ *   - the cache holds, per tensor, num_blocks x num_kv_heads tiles, each the
+ *     block_size x head_dim elements of one KV head's share of a block, and
+ *     slot s names block s / block_size, offset s % block_size; a negative
+ *     slot is padding and writes nothing.  Inside a tile (bs tokens, D dims,
+ *     E = 16 / element size dims per 16-byte chunk) K element (t, d) sits at
+ *     ((d / E) * bs + t) * E + d % E and V element (t, d) at
+ *     ((t / 4) * D + d) * 4 + t % 4.
  *
  * Precision: inputs are upcast exactly (fp32 -> double; bf16 -> fp32 by a
  * 16-bit shift -> double).  All arithmetic is IEEE double with sums taken
@@ -262,20 +266,29 @@ int oracle_append(const void *k, const void *v, const int32_t *slots, int T, int
 {
     if (T < 0 || Hkv <= 0 || D <= 0 || bs <= 0 || (elem_size != 2 && elem_size != 4))
         return -1;
+    const int E = 16 / elem_size;
+    if (D % E != 0 || bs % 4 != 0)
+        return -1;
     for (int t = 0; t < T; ++t)
         if (slots[t] >= 0 && (int64_t)slots[t] >= num_blocks * bs)
             return -1;
-    const size_t row = (size_t)D * (size_t)elem_size;
+    const size_t tile = (size_t)bs * (size_t)D;          /* elements per (block, head) tile */
     for (int t = 0; t < T; ++t) {
         int64_t s = slots[t];
         if (s < 0)
             continue;
         int64_t blk = s / bs, off = s % bs;
         for (int g = 0; g < Hkv; ++g) {
-            size_t src = ((size_t)t * Hkv + g) * row;
-            size_t dst = ((((size_t)blk * Hkv + g) * bs) + (size_t)off) * row;
-            memcpy((char *)k_cache + dst, (const char *)k + src, row);
-            memcpy((char *)v_cache + dst, (const char *)v + src, row);
+            size_t base = ((size_t)blk * Hkv + g) * tile;
+            for (int d = 0; d < D; ++d) {
+                size_t src = ((size_t)t * Hkv + g) * D + d;
+                size_t kdst = base + ((size_t)(d / E) * bs + off) * E + d % E;
+                size_t vdst = base + ((size_t)(off / 4) * D + d) * 4 + off % 4;
+                memcpy((char *)k_cache + kdst * elem_size, (const char *)k + src * elem_size,
+                       elem_size);
+                memcpy((char *)v_cache + vdst * elem_size, (const char *)v + src * elem_size,
+                       elem_size);
+            }
         }
     }
     return 0;

@@ -261,21 +261,49 @@ def test_prefill_zero_prior_first_row_is_v0():
 # Append: a tiny cache image written out by hand, plus invariants.
 
 def test_append_tiny_image_by_hand():
-    # 3 blocks x 2 KV heads x block 2 x D 2, float32; slots [3, -1, 0].
-    # slot 3 -> block 1, offset 1; slot 0 -> block 0, offset 0; -1 writes nothing.
-    k = np.array([[[1, 2], [3, 4]], [[5, 6], [7, 8]], [[9, 10], [11, 12]]], dtype=np.float32)
+    # 2 blocks x 1 KV head x block 4 x D 4, float32 (E = 4 dims per chunk,
+    # so a K tile is row-major and a V tile is its transpose); slots
+    # [5, -1, 0]: slot 5 -> block 1, offset 1; slot 0 -> block 0, offset 0.
+    k = np.array([[[1, 2, 3, 4]], [[5, 6, 7, 8]], [[9, 10, 11, 12]]], dtype=np.float32)
     v = -k
-    kc = np.full((3, 2, 2, 2), 99.0, dtype=np.float32)
-    vc = np.full((3, 2, 2, 2), 99.0, dtype=np.float32)
-    oracle.append(k, v, [3, -1, 0], kc, vc, 2)
-    exp = np.full((3, 2, 2, 2), 99.0, dtype=np.float32)
-    exp[1, 0, 1] = [1, 2]
-    exp[1, 1, 1] = [3, 4]
-    exp[0, 0, 0] = [9, 10]
-    exp[0, 1, 0] = [11, 12]
-    assert np.array_equal(kc, exp)
-    expv = np.where(exp == 99.0, 99.0, -exp).astype(np.float32)
-    assert np.array_equal(vc, expv)
+    kc = np.full((2, 1, 4, 4), 99.0, dtype=np.float32)
+    vc = np.full((2, 1, 4, 4), 99.0, dtype=np.float32)
+    oracle.append(k, v, [5, -1, 0], kc, vc, 4)
+    ek = np.full(32, 99.0, dtype=np.float32)
+    ek[16 + 4:16 + 8] = [1, 2, 3, 4]          # block 1, token 1: K row 1 of the tile
+    ek[0:4] = [9, 10, 11, 12]                 # block 0, token 0: K row 0
+    ev = np.full(32, 99.0, dtype=np.float32)
+    ev[[16 + 1, 16 + 5, 16 + 9, 16 + 13]] = [-1, -2, -3, -4]   # block 1: V column 1
+    ev[[0, 4, 8, 12]] = [-9, -10, -11, -12]                     # block 0: V column 0
+    assert np.array_equal(kc.reshape(-1), ek)
+    assert np.array_equal(vc.reshape(-1), ev)
+
+
+def test_append_chunked_positions_by_hand():
+    # bf16, block 8, D 16 (E = 8): token 5 of block 0, dim 10 lands at
+    # K index ((10 // 8) * 8 + 5) * 8 + 2 = 106 and V index
+    # ((5 // 4) * 16 + 10) * 4 + 1 = 105 (worked by hand).
+    k = np.zeros((1, 1, 16), dtype=np.uint16)
+    v = np.zeros((1, 1, 16), dtype=np.uint16)
+    k[0, 0, 10] = 0x1234
+    v[0, 0, 10] = 0x5678
+    kc = np.zeros((1, 1, 8, 16), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    oracle.append(k, v, [5], kc, vc, 8)
+    assert np.flatnonzero(kc.reshape(-1)).tolist() == [106]
+    assert np.flatnonzero(vc.reshape(-1)).tolist() == [105]
+    assert kc.reshape(-1)[106] == 0x1234 and vc.reshape(-1)[105] == 0x5678
+    assert oracle.tile_index(5, 10, 8, 16, 2) == (106, 105)
+    # f32, block 16, D 8 (E = 4): token 9, dim 6 -> K (1 * 16 + 9) * 4 + 2 = 102,
+    # V (2 * 8 + 6) * 4 + 1 = 89.
+    assert oracle.tile_index(9, 6, 16, 8, 4) == (102, 89)
+
+
+def _row(cache_tile: np.ndarray, t: int, bs: int, D: int, which: int) -> np.ndarray:
+    flat = cache_tile.reshape(-1)
+    es = cache_tile.dtype.itemsize
+    return np.array([flat[oracle.tile_index(t, d, bs, D, es)[which]] for d in range(D)],
+                    dtype=cache_tile.dtype)
 
 
 def test_append_bits_preserved_and_nothing_else_touched():
@@ -293,13 +321,16 @@ def test_append_bits_preserved_and_nothing_else_touched():
     # Logical read-back: every appended row is found where its slot says.
     for t, s in enumerate(slots):
         if s >= 0:
-            assert np.array_equal(kc.reshape(nb, H, bs, D)[s // bs, :, s % bs], k[t])
-            assert np.array_equal(vc[s // bs, :, s % bs], v[t])
+            for h in range(H):
+                assert np.array_equal(_row(kc[s // bs, h], s % bs, bs, D, 0), k[t, h])
+                assert np.array_equal(_row(vc[s // bs, h], s % bs, bs, D, 1), v[t, h])
     # Untouched slots keep the poison in every head.
     used = set(int(s) for s in slots if s >= 0)
     for s in range(nb * bs):
         if s not in used:
-            assert np.all(kc[s // bs, :, s % bs] == synth.POISON_BF16)
+            for h in range(H):
+                assert np.all(_row(kc[s // bs, h], s % bs, bs, D, 0) == synth.POISON_BF16)
+                assert np.all(_row(vc[s // bs, h], s % bs, bs, D, 1) == synth.POISON_BF16)
 
 
 def test_append_rejects_out_of_range_slot():
@@ -330,7 +361,7 @@ def test_copy_blocks_preserves_logical_rows_through_append():
     # a -> c and b -> d, reading the sequence through [c, d] gives the rows
     # that were appended, in order, for every head.
     g = np.random.default_rng(11)
-    nb, H, bs, D, T = 8, 3, 4, 5, 7
+    nb, H, bs, D, T = 8, 3, 4, 16, 7
     k = g.integers(0, 2**16, size=(T, H, D), dtype=np.uint16)
     v = g.integers(0, 2**16, size=(T, H, D), dtype=np.uint16)
     blocks = [5, 2]
@@ -342,8 +373,9 @@ def test_copy_blocks_preserves_logical_rows_through_append():
     oracle.copy_blocks(kc, vc, dk, dv, blocks, [0, 7])
     new = [0, 7]
     for t in range(T):
-        assert np.array_equal(dk[new[t // bs], :, t % bs], k[t])
-        assert np.array_equal(dv[new[t // bs], :, t % bs], v[t])
+        for h in range(H):
+            assert np.array_equal(_row(dk[new[t // bs], h], t % bs, bs, D, 0), k[t, h])
+            assert np.array_equal(_row(dv[new[t // bs], h], t % bs, bs, D, 1), v[t, h])
     untouched = [b for b in range(nb) if b not in new]
     assert not dk[untouched].any() and not dv[untouched].any()
 
