@@ -2,11 +2,15 @@
 // section "The KV cache": each step appends the new token's K and V).
 //
 // Row t of k/v ([T][Hkv][D]) is copied bit for bit into slot s =
-// slot_mapping[t] of the caches ([num_blocks][Hkv][block_size][D]): block
-// s / block_size, offset s % block_size.  One thread moves one 16-byte chunk
-// of K and the matching chunk of V; consecutive threads cover consecutive
-// chunks of a row, so both the reads and the writes of a row are coalesced
-// 16-byte accesses.  HBM bound: 2 * T * Hkv * D * elem bytes each way.
+// slot_mapping[t] of the caches: block s / BS, offset o = s % BS, inside
+// the tile of KV head g (tiles are [num_blocks][Hkv], BS x D elements each).
+// Tile layout: K keeps each token's dims in 16-byte chunks, chunk c of
+// token o at (c * BS + o) * 16 bytes; V keeps groups of 4 tokens together
+// per dim, element (o, d) at ((o / 4) * D + d) * 4 + o % 4.  One thread
+// moves one 16-byte chunk of the K row (a single 16-byte store) and the
+// matching chunk of the V row (E element stores, E = 16 / element size);
+// consecutive threads cover consecutive chunks of a row, so the row reads
+// are coalesced.  HBM bound: 2 * T * Hkv * D * elem bytes each way.
 #include <hip/hip_runtime.h>
 
 #include "pkv_internal.h"
@@ -18,51 +22,71 @@ constexpr int kThreads = 256;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// ROWC: 16-byte chunks per (token, head) row; BS: block size.  All index
-// math is 32-bit; the host guarantees T * Hkv * ROWC and num_blocks * BS fit.
-template <int ROWC, int BS>
+// Store V chunk c (E consecutive dims of token offset o) into a V tile.
+template <int D, int ES, int BS>
+__device__ __forceinline__ void store_v_chunk(char *tile, int o, int c, const u32x4 &x)
+{
+    constexpr int E = 16 / ES;
+    const int base = (o / 4) * D * 4 + o % 4;          // element index of (o, d = 0)
+    if constexpr (ES == 4) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            reinterpret_cast<uint32_t *>(tile)[base + (c * E + e) * 4] = x[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            reinterpret_cast<uint16_t *>(tile)[base + (c * E + e) * 4] =
+                (uint16_t)(x[e / 2] >> (16 * (e & 1)));
+    }
+}
+
+// All index math is 32-bit; the host guarantees T * Hkv * ROWC and
+// num_blocks * BS fit.
+template <int D, int ES, int BS>
 __global__ __launch_bounds__(kThreads) void k_append(const uint4 *__restrict__ k,
                                                      const uint4 *__restrict__ v,
                                                      const int32_t *__restrict__ slots,
-                                                     uint4 *__restrict__ kc, uint4 *__restrict__ vc,
+                                                     char *__restrict__ kc, char *__restrict__ vc,
                                                      int32_t total_chunks, int32_t heads,
                                                      int32_t cap_slots)
 {
-    const int32_t c = blockIdx.x * kThreads + threadIdx.x;
-    if (c >= total_chunks)
+    constexpr int ROWC = D * ES / 16;                   // 16-byte chunks per row
+    constexpr int TILE = BS * D * ES;                   // bytes per (block, head) tile
+    const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total_chunks)
         return;
-    const int32_t row = c / ROWC;          // (t, g) row of the input
-    const int32_t ch = c % ROWC;
+    const int32_t row = i / ROWC;                       // (t, g) row of the input
+    const int32_t c = i % ROWC;
     const int32_t t = row / heads;
     const int32_t g = row - t * heads;
     // The row loads do not depend on the slot: issue all three together so
     // the copy costs one memory latency, not two in a chain.
-    const u32x4 kk = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(k) + c);
-    const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(v) + c);
+    const u32x4 kk = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(k) + i);
+    const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(v) + i);
     const int32_t s = slots[t];
     asm volatile("" ::"v"(kk), "v"(vv));   // keep the row loads ahead of the branch
     if (s < 0 || s >= cap_slots)           // padding, or outside the cache: not written
         return;
-    const int32_t blk = s / BS, off = s % BS;
-    const int64_t dst = (((int64_t)blk * heads + g) * BS + off) * ROWC + ch;
-    reinterpret_cast<u32x4 *>(kc)[dst] = kk;
-    reinterpret_cast<u32x4 *>(vc)[dst] = vv;
+    const int32_t blk = s / BS, o = s % BS;
+    const int64_t tile = ((int64_t)blk * heads + g) * TILE;
+    *reinterpret_cast<u32x4 *>(kc + tile + (c * BS + o) * 16) = kk;
+    store_v_chunk<D, ES, BS>(vc + tile, o, c, vv);
 }
 
-template <int ROWC>
-int launch_rowc(const AppendLaunch &a, int32_t total, hipStream_t st)
+template <int D, int ES>
+int launch_shape(const AppendLaunch &a, int32_t total, hipStream_t st)
 {
     const unsigned grid = (unsigned)((total + kThreads - 1) / kThreads);
     const int32_t cap = a.num_blocks * a.block_size;
     auto kp = static_cast<const uint4 *>(a.k);
     auto vp = static_cast<const uint4 *>(a.v);
-    auto kc = static_cast<uint4 *>(a.k_cache);
-    auto vc = static_cast<uint4 *>(a.v_cache);
+    auto kc = static_cast<char *>(a.k_cache);
+    auto vc = static_cast<char *>(a.v_cache);
     if (a.block_size == 16)
-        hipLaunchKernelGGL((k_append<ROWC, 16>), dim3(grid), dim3(kThreads), 0, st, kp, vp,
+        hipLaunchKernelGGL((k_append<D, ES, 16>), dim3(grid), dim3(kThreads), 0, st, kp, vp,
                            a.slots, kc, vc, total, a.num_kv_heads, cap);
     else
-        hipLaunchKernelGGL((k_append<ROWC, 32>), dim3(grid), dim3(kThreads), 0, st, kp, vp,
+        hipLaunchKernelGGL((k_append<D, ES, 32>), dim3(grid), dim3(kThreads), 0, st, kp, vp,
                            a.slots, kc, vc, total, a.num_kv_heads, cap);
     return PKV_OK;
 }
@@ -78,11 +102,15 @@ int launch_append(const AppendLaunch &a)
     if (total > INT32_MAX || (int64_t)a.num_blocks * a.block_size > INT32_MAX)
         return fail(PKV_EINVAL, "pkv_append: too many tokens or slots for 32-bit indexing");
     hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-    switch (rowc) {
-    case 8: launch_rowc<8>(a, (int32_t)total, st); break;
-    case 16: launch_rowc<16>(a, (int32_t)total, st); break;
-    case 32: launch_rowc<32>(a, (int32_t)total, st); break;
-    default: return fail(PKV_EUNSUPPORTED, "pkv_append: row of %d bytes", rowc * 16);
+    const int key = a.head_dim * 10 + a.elem_size;
+    switch (key) {
+    case 642: launch_shape<64, 2>(a, (int32_t)total, st); break;
+    case 1282: launch_shape<128, 2>(a, (int32_t)total, st); break;
+    case 644: launch_shape<64, 4>(a, (int32_t)total, st); break;
+    case 1284: launch_shape<128, 4>(a, (int32_t)total, st); break;
+    default:
+        return fail(PKV_EUNSUPPORTED, "pkv_append: head_dim %d with %d-byte elements",
+                    a.head_dim, a.elem_size);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -1,5 +1,5 @@
-// Paged decode attention for gfx950 (CDNA4): a work-balanced split pass plus
-// a log-sum-exp merge pass.
+// Paged decode attention for gfx950 (CDNA4): a work-balanced split pass on
+// the matrix cores plus a log-sum-exp merge pass.
 //
 // What is computed ("LLM Inference: KV Cache, Batching & Scheduling",
 // sections "The KV cache" and "PagedAttention and vLLM"; the "LLM Inference
@@ -23,36 +23,38 @@
 // launch.)  The result depends only on the lengths and W, never on physical
 // block ids or scheduling.
 //
-// Inside a workgroup (one KV head g, one range):
-//   * 4 waves; for each piece (the part of one sequence inside the range)
-//     wave w takes blocks w, w+4, ... of the piece.  A wave is R rows of LPT
-//     lanes; lane (row r, i) loads the 16-byte chunk i of token rows r,
-//     r+R, ... of each K and V block tile: whole-block, coalesced 16-byte
-//     loads straight from HBM into registers, the next sub-tile's loads in
-//     flight while the current one is processed.
-//   * GQA packing: each lane keeps its 16-byte slice of q for all G query
-//     heads of the group, so every K/V byte read from HBM serves the G heads.
-//   * QK^T: per lane, partial dot products over its slice (bf16 pairs via
-//     v_dot2_f32_bf16, fp32 accumulation), then a cross-lane reduction by
-//     recursive halving with DPP row_mirror / row_half_mirror / quad_perm
-//     exchanges: lane i holds q heads in an order permuted by its own lane
-//     bits, so at every halving step the half a lane keeps and the half it
-//     sends sit in the same registers on every lane, and each step costs one
-//     DPP add per kept value.  Afterwards each lane owns the full scores of
-//     G / 2^S heads for its row's tokens.
-//   * Online softmax per (row, head) stream in log2 units (exp2 on the
-//     hardware exp unit); masking by select, never by multiplying, so NaN
-//     poison in unused slots never reaches the result.
-//   * PV: lane (r, i) accumulates o[h][its 8 (bf16) or 4 (fp32) dims] for all
-//     G heads with p broadcast from the owning lane by DPP row_newbcast.
-//   * End of a piece: the R row streams of a wave merge in registers with
-//     cross-row lane swaps (v_permlane16/32_swap, DPP row_ror), the 4 waves
-//     through a 16 KiB LDS buffer.
+// Inside a workgroup (one KV head g, one range), 4 waves; for each piece
+// (the part of one sequence inside the range) wave w takes blocks w, w+4, ...
+// of the piece, each as units of 16 tokens.  Lane l of a wave is
+// (quarter g4 = l / 16, column n = l % 16); column n stands for query head
+// g*G + n (columns n >= G are idle padding).
+//   * Loads.  The cache tile layout makes every 16-byte load of a wave one
+//     coalesced run that lands directly in a matrix-core operand: K keeps
+//     each token's dims in 16-byte chunks (chunk c of token t at
+//     (c * bs + t) * 16 bytes), so load kk gives lane l chunk 4 kk + g4 of
+//     token n; V keeps 4 consecutive tokens of one dim together, so a load
+//     gives lane l tokens 4 g4 .. 4 g4 + 3 of one or two dims.  Loads go
+//     through buffer resources on the (block, head) tile; an id outside the
+//     pool gets an empty resource and reads zeros without touching memory.
+//     Three register buffers rotate: units e+1 and e+2 are in flight while
+//     unit e is computed.
+//   * S = K Q^T on MFMA (bf16: v_mfma_f32_16x16x32_bf16, A = the K chunks as
+//     loaded, B = the group's q rows, zero for padding columns; fp32:
+//     v_mfma_f32_16x16x4_f32).  Lane l gets S for tokens 4 g4 .. 4 g4 + 3 of
+//     head n.
+//   * Online softmax per head in log2 units: the unit max reduced over the 4
+//     quarters (v_permlane16/32_swap), a lazy running max (rescale only when
+//     the max grows by more than 2^8), masking by select so NaN poison in
+//     unused slots never reaches the result.
+//   * O^T += V^T P^T on MFMA: the S layout is already the B-operand layout
+//     of P^T, so P never leaves its lane.  bf16: P is split into bf16 high
+//     and low parts (two v_mfma_f32_16x16x16_bf16), keeping ~16 significant
+//     bits of each weight; fp32: v_mfma_f32_16x16x4_f32 on P as is.
+//   * End of a piece: per head the quarters' sums are added, and the 4
+//     waves merge through LDS.
 //   * Grid (Hkv, W) with the KV head fastest, so workgroups of one KV head
 //     land on one XCD and blocks shared between sequences stay in its L2.
 #include <hip/hip_runtime.h>
-
-#include <utility>
 
 #include "pkv_internal.h"
 
@@ -65,9 +67,11 @@ constexpr float kLazyMax = 8.0f;      // running-max slack, log2 units
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data format, no swizzle
 constexpr int kIdChunk = 512;         // block-table entries staged in LDS at a time
 
-constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
-
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct Args {
     const void *q;
@@ -84,8 +88,9 @@ struct Args {
     const int32_t *slots;             // fused append: slot of sequence b's new row
     void *kc_w;                       // the caches, written by the fused append
     void *vc_w;
-    int32_t row_chunks;               // 16-byte chunks per K/V row (LPT)
+    int32_t row_chunks;               // 16-byte chunks per K/V row
     int32_t block_size;
+    int32_t head_dim;
     int32_t stride;
     int32_t B, Hq, Hkv, num_blocks;
     int32_t W;                        // workgroups per KV head
@@ -96,136 +101,19 @@ struct Args {
 
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// Value held by lane (i ^ C) inside groups of C + 1 lanes.
-template <int C>
-__device__ __forceinline__ float xmirror(float v)
-{
-    if constexpr (C == 1)
-        return __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-    else if constexpr (C == 3)
-        return __builtin_amdgcn_update_dpp(0.0f, v, 0x1B, 0xF, 0xF, false);   // quad_perm 3,2,1,0
-    else if constexpr (C == 7)
-        return __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    else if constexpr (C == 15)
-        return __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, false);  // row_mirror
-    else {
-        static_assert(C == 31, "mirror width");
-        // ds_swizzle bit mode: and 0x1f, or 0, xor 0x1f (within 32 lanes)
-        return __builtin_bit_cast(float,
-                                  __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x7C1F));
-    }
-}
-
-// Value held by lane SRC of this lane's group of LPT lanes.
-template <int LPT, int SRC>
-__device__ __forceinline__ float bcast(float v)
-{
-    if constexpr (LPT == 16)   // row_newbcast; every lane is written, so no old value
-        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
-                                                                  0x150 + SRC, 0xF, 0xF, true));
-    else if constexpr (LPT == 8)
-        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                                     (SRC << 5) | 0x18));
-    else {
-        static_assert(LPT == 32, "group width");
-        return __builtin_bit_cast(float,
-                                  __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SRC << 5));
-    }
-}
-
 template <int DT, int D, int BS, int G>
 struct Shape {
     static constexpr int ES = DT == PKV_F32 ? 4 : 2;   // element bytes
-    static constexpr int CH = 16 / ES;                 // elements per 16-byte chunk
-    static constexpr int LPT = D / CH;                 // lanes per token row
-    static constexpr int R = 64 / LPT;                 // token rows per wave
-    static constexpr int SUBTOK = BS < 4 * R ? BS : 4 * R;   // tokens per pipelined sub-tile
-    static constexpr int NSUBT = BS / SUBTOK;          // sub-tiles per block
-    static constexpr int TPR = SUBTOK / R;             // tokens per row per sub-tile (<= 4)
-    static constexpr int LL = ilog2(LPT);
-    static constexpr int LG = ilog2(G);
-    static constexpr int S = LG < LL ? LG : LL;        // halving steps
-    static constexpr int GH = G >> S;                  // heads a lane owns after reduction
-    static constexpr int NSUB = NW * R;                // softmax streams per workgroup
-    static_assert(TPR >= 1 && (1 << LL) == LPT && (1 << LG) == G, "shape");
+    static constexpr int E = 16 / ES;                  // dims per 16-byte chunk
+    static constexpr int LPT = D / E;                  // chunks per K / q row
+    static constexpr int NKL = LPT / 4;                // K loads per lane per unit
+    static constexpr int NVL = DT == PKV_F32 ? D / 16 : D / 32;   // V loads per lane per unit
+    static constexpr int NACC = D / 16;                // O^T accumulator tiles
+    static constexpr int NSUB = BS / 16;               // 16-token units per block
+    static constexpr int TILE = BS * D * ES;           // bytes of one (block, head) tile
+    static constexpr int OSTR = D + 4;                 // LDS row stride of a wave's output
+    static_assert(NKL >= 1 && NSUB >= 1 && G <= 16, "shape");
 };
-
-// Recursive halving of the G x TPR partial scores across the LPT lanes of a
-// row; step s keeps heads [0, G >> (s+1)) and adds the partner's copy of the
-// same heads, which the partner holds in registers h ^ X.
-template <int s, int S, int LL, int LG, int G, int TPR>
-__device__ __forceinline__ void halve(float (&acc)[G][TPR])
-{
-    if constexpr (s < S) {
-        constexpr int X = ((1 << (LG - s)) - 1) ^ ((1 << (LG - S)) - 1);
-        constexpr int C = (1 << (LL - s)) - 1;
-#pragma unroll
-        for (int h = 0; h < (G >> (s + 1)); ++h)
-#pragma unroll
-            for (int t = 0; t < TPR; ++t)
-                acc[h][t] += xmirror<C>(acc[h ^ X][t]);
-        halve<s + 1, S, LL, LG, G, TPR>(acc);
-    }
-}
-
-// Plain butterfly over the lane bits the halving did not use.
-template <int bit, int GH, int G, int TPR>
-__device__ __forceinline__ void butterfly(float (&acc)[G][TPR])
-{
-    if constexpr (bit >= 0) {
-        constexpr int C = (1 << (bit + 1)) - 1;
-#pragma unroll
-        for (int h = 0; h < GH; ++h)
-#pragma unroll
-            for (int t = 0; t < TPR; ++t)
-                acc[h][t] += xmirror<C>(acc[h][t]);
-        butterfly<bit - 1, GH, G, TPR>(acc);
-    }
-}
-
-// Partial dot product of one 16-byte chunk of q and of k.
-template <int DT>
-__device__ __forceinline__ float chunk_dot(const uint4 &q, const uint4 &k)
-{
-    if constexpr (DT == PKV_BF16) {
-        // First pair through the VOP3P form with an inline zero accumulator
-        // (the compiler would otherwise zero a register for v_dot2c).
-        float a;
-        asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(a) : "v"(q.x), "v"(k.x));
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y),
-                                            __builtin_bit_cast(bf16x2_t, k.y), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z),
-                                            __builtin_bit_cast(bf16x2_t, k.z), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w),
-                                            __builtin_bit_cast(bf16x2_t, k.w), a, false);
-        return a;
-    } else {
-        float a = as_f32(q.x) * as_f32(k.x);
-        a = __builtin_fmaf(as_f32(q.y), as_f32(k.y), a);
-        a = __builtin_fmaf(as_f32(q.z), as_f32(k.z), a);
-        a = __builtin_fmaf(as_f32(q.w), as_f32(k.w), a);
-        return a;
-    }
-}
-
-// The 16-byte chunk of v as CH floats.
-template <int DT>
-__device__ __forceinline__ void chunk_to_f32(const uint4 &v, float (&f)[16 / (DT == PKV_F32 ? 4 : 2)])
-{
-    if constexpr (DT == PKV_BF16) {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            f[2 * c] = as_f32(w[c] << 16);
-            f[2 * c + 1] = as_f32(w[c] & 0xFFFF0000u);
-        }
-    } else {
-        f[0] = as_f32(v.x);
-        f[1] = as_f32(v.y);
-        f[2] = as_f32(v.z);
-        f[3] = as_f32(v.w);
-    }
-}
 
 __device__ __forceinline__ uint16_t bf16_rne(float f)
 {
@@ -242,6 +130,33 @@ __device__ __forceinline__ void store_out(void *out, int32_t dtype, int64_t idx,
         static_cast<float *>(out)[idx] = x;
     else
         static_cast<uint16_t *>(out)[idx] = bf16_rne(x);
+}
+
+// Write chunk i (16 bytes) of sequence b's new K (kv = 0) or V (kv = 1) row
+// of KV head g into slot nslot of the caches (fused append), in the tile
+// layout: K chunk i of token o at (i * bs + o) * 16 bytes, V element (o, d)
+// at ((o / 4) * D + d) * 4 + o % 4.
+__device__ __forceinline__ void store_new_chunk(const Args &a, int nslot, int g, int kv, int i,
+                                                const uint4 &row)
+{
+    const int bs = a.block_size, D = a.head_dim;
+    const int E = D / a.row_chunks, es = 16 / E;
+    const int blk = nslot / bs, o = nslot % bs;
+    char *tile = static_cast<char *>(kv ? a.vc_w : a.kc_w) +
+                 ((int64_t)blk * a.Hkv + g) * ((int64_t)bs * D * es);
+    if (kv == 0) {
+        *reinterpret_cast<uint4 *>(tile + (i * bs + o) * 16) = row;
+        return;
+    }
+    const uint32_t w[4] = {row.x, row.y, row.z, row.w};
+    const int base = (o / 4) * D * 4 + o % 4;
+    for (int e = 0; e < E; ++e) {
+        const int idx = base + (i * E + e) * 4;
+        if (es == 4)
+            reinterpret_cast<uint32_t *>(tile)[idx] = w[e];
+        else
+            reinterpret_cast<uint16_t *>(tile)[idx] = (uint16_t)(w[e / 2] >> (16 * (e & 1)));
+    }
 }
 
 // Combine v with the value of lane (l ^ X) (X = 8, 16 or 32) by + or max;
@@ -304,24 +219,22 @@ template <int DT, int D, int BS, int G>
 __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
 {
     using Sh = Shape<DT, D, BS, G>;
-    constexpr int CH = Sh::CH, LPT = Sh::LPT, R = Sh::R, TPR = Sh::TPR;
-    constexpr int SUBTOK = Sh::SUBTOK, NSUBT = Sh::NSUBT;
-    constexpr int LL = Sh::LL, LG = Sh::LG, S = Sh::S, GH = Sh::GH;
-    constexpr int TILE = BS * D * Sh::ES;              // bytes of one (block, head) tile
+    constexpr int LPT = Sh::LPT, NKL = Sh::NKL, NVL = Sh::NVL, NACC = Sh::NACC;
+    constexpr int NSUB = Sh::NSUB, TILE = Sh::TILE, OSTR = Sh::OSTR;
 
     __shared__ int32_t lds_pref[kDecodeMaxSeqs + 1];
     __shared__ __attribute__((aligned(16))) uint4 lds_q[G * LPT];
     __shared__ __attribute__((aligned(16))) uint4 lds_new[2][LPT];   // fused append: K, V row
     __shared__ int32_t lds_ids[kIdChunk];
     __shared__ int32_t lds_wsum[NW];
-    __shared__ float lds_o[NW][G * D];
+    __shared__ float lds_o[NW][G * OSTR];
     __shared__ float lds_m[NW][G];
     __shared__ float lds_l[NW][G];
 
     const int g = blockIdx.x, wg = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane / LPT, li = lane % LPT;
+    const int g4 = lane >> 4, n = lane & 15;
 
     // Prefix sums of the per-sequence block counts (the same in every
     // workgroup).
@@ -378,11 +291,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
         b = lo;
     }
 
-    const int hm = (li >> (LL - S)) << (LG - S);   // this lane's head permutation
     const int64_t blk_bytes = (int64_t)a.Hkv * TILE;
     const char *kbase = static_cast<const char *>(a.kc) + (int64_t)g * TILE;
     const char *vbase = static_cast<const char *>(a.vc) + (int64_t)g * TILE;
-    const uint32_t lane_off = (uint32_t)lane * 16u;
+    // This lane's byte offsets inside a tile: K load kk of unit h, V load u.
+    const uint32_t koff = (uint32_t)((g4 * BS + n) * 16);
+    const uint32_t voff = DT == PKV_F32 ? (uint32_t)((g4 * D + n) * 16)
+                                        : (uint32_t)((g4 * D + 2 * n) * 8);
 
     int64_t x = start;
     while (x < end) {
@@ -395,9 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
         const int nblk = se - sb;
         const int32_t *bt = a.tables + (int64_t)b * a.stride;
 
-        // The group's q rows go to LDS (G * D elements); each lane reads its
-        // slices from there when it needs them, heads permuted by its own
-        // lane bits: slot h holds query head g*G + (h ^ hm).
+        // The group's q rows (G * D elements) go to LDS.
         {
             const uint4 *qp = static_cast<const uint4 *>(a.q) + ((int64_t)b * a.Hq + hq0) * LPT;
             for (int i = tid; i < G * LPT; i += kThreads)
@@ -414,162 +327,213 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
             const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
                 [((int64_t)b * a.Hkv + g) * LPT + i];
             lds_new[kv][i] = row;
-            const int64_t dst = (((int64_t)(nslot / BS) * a.Hkv + g) * BS + nslot % BS) * LPT + i;
-            static_cast<uint4 *>(kv ? a.vc_w : a.kc_w)[dst] = row;
+            store_new_chunk(a, nslot, g, kv, i, row);
         }
         __syncthreads();
 
-        float o[G][CH];
+        // This lane's B operand of S = K Q^T: chunk 4 kk + g4 of query head
+        // n's row (zero for the padding columns n >= G).
+        uint4 qr[NKL];
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int kk = 0; kk < NKL; ++kk)
+            qr[kk] = n < G ? lds_q[n * LPT + 4 * kk + g4] : make_uint4(0, 0, 0, 0);
+
+        f32x4 o[NACC];
 #pragma unroll
-            for (int c = 0; c < CH; ++c)
-                o[h][c] = 0.0f;
-        float m[GH], l[GH];
-#pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            m[h] = -INFINITY;
-            l[h] = 0.0f;
-        }
+        for (int i = 0; i < NACC; ++i)
+            o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float m = -INFINITY, l = 0.0f;
 
         int c0 = j0;                       // first block of the staged id chunk
-        auto blk_of = [&](int e) { return c0 + w + (e / NSUBT) * NW; };
+        auto blk_of = [&](int e) { return c0 + w + (e / NSUB) * NW; };
 
-        // Issue the 2 * TPR 16-byte loads of one sub-tile through a buffer
-        // resource whose base is the wave-uniform tile address (scalar
-        // registers) and this lane's fixed 32-bit offset.  A block id outside
-        // the pool gets an empty resource, so its loads return zeros without
-        // touching memory; every load is unconditional and the wait counts
-        // stay exact.
-        auto issue = [&](int e, int id, uint4 (&kr)[TPR], uint4 (&vr)[TPR]) {
+        // Issue the loads of unit e (16 tokens of one block): NKL K chunks
+        // and NVL V chunks per lane, through buffer resources on the block's
+        // tile (scalar registers) with this lane's fixed offsets.  Loads past
+        // the last unit, or of an id outside the pool, go through an empty
+        // resource (zeros, no memory access), so every iteration issues the
+        // same loads and the compiler's wait counts stay exact.
+        auto issue = [&](int e, int id, uint4 (&kr)[NKL], uint4 (&vr)[NVL]) {
             const bool ok = (unsigned)id < (unsigned)a.num_blocks;
-            const int64_t off = (int64_t)(ok ? id : 0) * blk_bytes + (e % NSUBT) * (TPR * 1024);
-            const int nrec = ok ? TPR * 1024 : 0;
+            const int64_t off = (int64_t)(ok ? id : 0) * blk_bytes;
+            const int nrec = ok ? TILE : 0;
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(kbase + off), 0, nrec, kRsrcWord3);
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<char *>(vbase + off), 0, nrec, kRsrcWord3);
+            const int h = e % NSUB;
 #pragma unroll
-            for (int t = 0; t < TPR; ++t) {
-                kr[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rk, (int)(lane_off + t * 1024u), 0, 0));
-                vr[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rv, (int)(lane_off + t * 1024u), 0, 0));
+            for (int kk = 0; kk < NKL; ++kk)
+                kr[kk] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rk, (int)(koff + (uint32_t)((4 * kk * BS + 16 * h) * 16)), 0, 0));
+#pragma unroll
+            for (int u = 0; u < NVL; ++u) {
+                const uint32_t c = DT == PKV_F32 ? (uint32_t)((4 * h * D + 16 * u) * 16)
+                                                 : (uint32_t)((4 * h * D + 32 * u) * 8);
+                vr[u] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + c), 0, 0));
             }
         };
 
-        // One sub-tile: QK^T, online softmax update, PV.
-        auto process = [&](int e, int id, uint4 (&kr)[TPR], uint4 (&vr)[TPR]) {
+        // One unit: S = K Q^T, online softmax update, O^T += V^T P^T.
+        auto process = [&](int e, int id, uint4 (&kr)[NKL], uint4 (&vr)[NVL]) {
             const int j = blk_of(e);
+            const int ubase = j * BS + 16 * (e % NSUB);     // position of the unit's token 0
             const bool ok = (unsigned)id < (unsigned)a.num_blocks;
-            if (fresh && j == nblk - 1) {
-                const int pl = j * BS + (e % NSUBT) * SUBTOK + r;   // position of token row 0
+            if (fresh && j == nblk - 1 && L - 1 >= ubase && L - 1 < ubase + 16) {
+                const int t = L - 1 - ubase;                 // the new row's token in the unit
+                if (n == t) {
 #pragma unroll
-                for (int t = 0; t < TPR; ++t)
-                    if (pl + t * R == L - 1) {
-                        kr[t] = lds_new[0][li];
-                        vr[t] = lds_new[1][li];
+                    for (int kk = 0; kk < NKL; ++kk)
+                        kr[kk] = lds_new[0][4 * kk + g4];
+                }
+                if (g4 == (t >> 2)) {
+                    const int ti = t & 3;
+#pragma unroll
+                    for (int u = 0; u < NVL; ++u) {
+                        if constexpr (DT == PKV_F32) {
+                            const uint32_t nv = reinterpret_cast<const uint32_t *>(lds_new[1])
+                                [16 * u + n];
+                            if (ti == 0) vr[u].x = nv;
+                            else if (ti == 1) vr[u].y = nv;
+                            else if (ti == 2) vr[u].z = nv;
+                            else vr[u].w = nv;
+                        } else {
+                            const uint16_t *nr = reinterpret_cast<const uint16_t *>(lds_new[1]);
+                            const uint32_t n0 = nr[32 * u + 2 * n], n1 = nr[32 * u + 2 * n + 1];
+                            const int sh = 16 * (ti & 1);
+                            const uint32_t keep = ~(0xFFFFu << sh);
+                            if (ti < 2) {
+                                vr[u].x = (vr[u].x & keep) | (n0 << sh);
+                                vr[u].z = (vr[u].z & keep) | (n1 << sh);
+                            } else {
+                                vr[u].y = (vr[u].y & keep) | (n0 << sh);
+                                vr[u].w = (vr[u].w & keep) | (n1 << sh);
+                            }
+                        }
                     }
+                }
             }
-            float acc[G][TPR];
+
+            // S for tokens 4 g4 .. 4 g4 + 3 of head n.
+            f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const uint4 qh = lds_q[(h ^ hm) * LPT + li];
-#pragma unroll
-                for (int t = 0; t < TPR; ++t)
-                    acc[h][t] = chunk_dot<DT>(qh, kr[t]);
+            for (int kk = 0; kk < NKL; ++kk) {
+                if constexpr (DT == PKV_F32) {
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].x), as_f32(qr[kk].x),
+                                                                sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].y), as_f32(qr[kk].y),
+                                                                sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].z), as_f32(qr[kk].z),
+                                                                sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].w), as_f32(qr[kk].w),
+                                                                sacc, 0, 0, 0);
+                } else {
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, kr[kk]), __builtin_bit_cast(bf16x8, qr[kk]),
+                        sacc, 0, 0, 0);
+                }
             }
-            halve<0, S, LL, LG, G, TPR>(acc);
-            butterfly<LL - S - 1, GH, G, TPR>(acc);
 
             // Scores in log2 units; positions past the context are masked.
-            // The running max only moves when a block's max exceeds it by
-            // more than 2^8: exponentials stay <= 256, and the rescale of o
-            // is skipped unless some stream of the wave moved.
-            const int pos0 = j * BS + (e % NSUBT) * SUBTOK + r;
+            const int pos0 = ubase + 4 * g4;
             const bool full = ok && (j + 1) * BS <= L;      // wave-uniform
-            float p[GH][TPR], alpha[GH];
-            bool grew = false;
+            float s[4];
 #pragma unroll
-            for (int h = 0; h < GH; ++h)
-#pragma unroll
-                for (int t = 0; t < TPR; ++t)
-                    p[h][t] = acc[h][t] * a.scale_log2;
+            for (int i = 0; i < 4; ++i)
+                s[i] = sacc[i] * a.scale_log2;
             if (!full) {
 #pragma unroll
-                for (int h = 0; h < GH; ++h)
-#pragma unroll
-                    for (int t = 0; t < TPR; ++t)
-                        p[h][t] = (ok && pos0 + t * R < L) ? p[h][t] : -INFINITY;
+                for (int i = 0; i < 4; ++i)
+                    s[i] = (ok && pos0 + i < L) ? s[i] : -INFINITY;
             }
+            float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            mt = xrow<16, true>(mt);
+            mt = xrow<32, true>(mt);
+            const bool up = mt > m + kLazyMax;
+            const float mn = up ? mt : m;
+            const float alpha = up ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+            const bool dead = (mn == -INFINITY);
+            float p[4], sum = 0.0f;
 #pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                float mb = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                p[i] = dead ? 0.0f : __builtin_amdgcn_exp2f(s[i] - mn);
+                sum += p[i];
+            }
+            l = __builtin_fmaf(l, alpha, sum);
+            m = mn;
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {
 #pragma unroll
-                for (int t = 0; t < TPR; ++t)
-                    mb = fmaxf(mb, p[h][t]);
-                const bool up = mb > m[h] + kLazyMax;
-                const float mn = up ? mb : m[h];
-                alpha[h] = up ? __builtin_amdgcn_exp2f(m[h] - mn) : 1.0f;
-                grew |= up;
-                const bool dead = (mn == -INFINITY);
-                float sum = 0.0f;
+                for (int i = 0; i < NACC; ++i)
+                    o[i] *= alpha;
+            }
+
+            // Unused slots past the context end hold arbitrary bits (NaN
+            // poison): zero their V so that 0 * NaN never reaches the sum.
+            if (!full && ok) {
+                const int nv = L - pos0;                     // valid tokens of this quarter
 #pragma unroll
-                for (int t = 0; t < TPR; ++t) {
-                    p[h][t] = dead ? 0.0f : __builtin_amdgcn_exp2f(p[h][t] - mn);
-                    sum += p[h][t];
+                for (int u = 0; u < NVL; ++u) {
+                    if constexpr (DT == PKV_F32) {
+                        vr[u].x = nv > 0 ? vr[u].x : 0u;
+                        vr[u].y = nv > 1 ? vr[u].y : 0u;
+                        vr[u].z = nv > 2 ? vr[u].z : 0u;
+                        vr[u].w = nv > 3 ? vr[u].w : 0u;
+                    } else {
+                        const uint32_t m01 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+                        const uint32_t m23 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+                        vr[u].x &= m01;
+                        vr[u].y &= m23;
+                        vr[u].z &= m01;
+                        vr[u].w &= m23;
+                    }
                 }
-                l[h] = __builtin_fmaf(l[h], alpha[h], sum);
-                m[h] = mn;
             }
 
-            // Rescale the accumulators of every head by its owner's alpha.
-            if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-                [&]<int... H>(std::integer_sequence<int, H...>) {
-                    (([&] {
-                         constexpr int src = (H >> (LG - S)) << (LL - S);
-                         const float ah = bcast<LPT, src>(alpha[H & (GH - 1)]);
+            // O^T += V^T P^T.
+            if constexpr (DT == PKV_F32) {
 #pragma unroll
-                         for (int c = 0; c < CH; ++c)
-                             o[H][c] *= ah;
-                     }()),
-                     ...);
-                }(std::make_integer_sequence<int, G>{});
-            }
-
-            // The context's last block may hold unused slots, and a bad id
-            // reads as zeros: such V must not reach the sum (0 * NaN would).
-            if (j == nblk - 1 || !ok) {
+                for (int u = 0; u < NVL; ++u) {
+                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].x), p[0], o[u], 0, 0, 0);
+                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].y), p[1], o[u], 0, 0, 0);
+                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].z), p[2], o[u], 0, 0, 0);
+                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].w), p[3], o[u], 0, 0, 0);
+                }
+            } else {
+                // hi = p truncated to bf16 (its top 16 bits, exact in fp32),
+                // lo = bf16(p - hi).
+                uint32_t pu[4];
 #pragma unroll
-                for (int t = 0; t < TPR; ++t)
-                    if (!ok || pos0 + t * R >= L)
-                        vr[t] = make_uint4(0, 0, 0, 0);
-            }
-
-            // PV with p broadcast from the lane that owns the head.
+                for (int i = 0; i < 4; ++i)
+                    pu[i] = __builtin_bit_cast(uint32_t, p[i]);
+                const uint32_t h01 = __builtin_amdgcn_perm(pu[1], pu[0], 0x07060302u);
+                const uint32_t h23 = __builtin_amdgcn_perm(pu[3], pu[2], 0x07060302u);
+                const uint32_t l01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                    f32x2{p[0] - as_f32(pu[0] & 0xFFFF0000u), p[1] - as_f32(pu[1] & 0xFFFF0000u)},
+                    bf16x2_t));
+                const uint32_t l23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                    f32x2{p[2] - as_f32(pu[2] & 0xFFFF0000u), p[3] - as_f32(pu[3] & 0xFFFF0000u)},
+                    bf16x2_t));
+                const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
+                const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
 #pragma unroll
-            for (int t = 0; t < TPR; ++t) {
-                float vf[CH];
-                chunk_to_f32<DT>(vr[t], vf);
-                [&]<int... H>(std::integer_sequence<int, H...>) {
-                    (([&] {
-                         constexpr int src = (H >> (LG - S)) << (LL - S);
-                         const float ph = bcast<LPT, src>(p[H & (GH - 1)][t]);
-#pragma unroll
-                         for (int c = 0; c < CH; ++c)
-                             o[H][c] = __builtin_fmaf(ph, vf[c], o[H][c]);
-                     }()),
-                     ...);
-                }(std::make_integer_sequence<int, G>{});
+                for (int u = 0; u < NVL; ++u) {
+                    const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[u].x, vr[u].y));
+                    const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[u].z, vr[u].w));
+                    o[2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, phi, o[2 * u], 0, 0, 0);
+                    o[2 * u + 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v1, phi, o[2 * u + 1], 0, 0, 0);
+                    o[2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, plo, o[2 * u], 0, 0, 0);
+                    o[2 * u + 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v1, plo, o[2 * u + 1], 0, 0, 0);
+                }
             }
         };
 
         // Wave w takes blocks j0 + w, j0 + w + NW, ... of the piece, each as
-        // NSUBT sub-tiles (units e = 0 .. E-1).  Three register buffers
-        // rotate: the loads of units e+1 and e+2 are in flight while unit e
-        // is processed.  Loads past the last unit go through an empty
-        // resource (zeros, no memory access), so every iteration issues the
-        // same loads and the compiler's wait counts stay exact.
+        // NSUB units (e = 0 .. E-1).  Three register buffers rotate: the
+        // loads of units e+1 and e+2 are in flight while unit e is computed.
         // The piece's block ids are staged through LDS in chunks, so the
         // loop issues no vector-memory reads besides the K/V tiles: a table
         // read would share the in-order load counter with them and waiting
@@ -580,12 +544,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
               lds_ids[i] = bt[c0 + i];
           __syncthreads();
           if (c0 + w < c1) {
-            const int E = ((c1 - c0 - w + NW - 1) / NW) * NSUBT;
+            const int E = ((c1 - c0 - w + NW - 1) / NW) * NSUB;
             auto id_of = [&](int e) {
-                const int id = lds_ids[(e < E ? e : E - 1) / NSUBT * NW + w];
+                const int id = lds_ids[(e < E ? e : E - 1) / NSUB * NW + w];
                 return e < E ? id : -1;
             };
-            uint4 kA[TPR], vA[TPR], kB[TPR], vB[TPR], kC[TPR], vC[TPR];
+            uint4 kA[NKL], vA[NVL], kB[NKL], vB[NVL], kC[NKL], vC[NVL];
             int idA = id_of(0), idB = id_of(1), idC = id_of(2), idn;
             issue(0, idA, kA, vA);
             issue(1, idB, kB, vB);
@@ -613,38 +577,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
           __syncthreads();
         }
 
-        // Merge the R row streams of the wave in registers: per head, the
-        // row's (m, l) from its owning lane, the wave max, then every row's
-        // share rescaled and summed across rows.
-        float mw[G], lw[G];
-        [&]<int... H>(std::integer_sequence<int, H...>) {
-            (([&] {
-                 constexpr int src = (H >> (LG - S)) << (LL - S);
-                 const float mr = bcast<LPT, src>(m[H & (GH - 1)]);
-                 const float lr = bcast<LPT, src>(l[H & (GH - 1)]);
-                 const float M = rows_reduce<LPT, true>(mr);
-                 const float f = (mr == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mr - M);
-                 lw[H] = rows_reduce<LPT, false>(lr * f);
-                 mw[H] = M;
+        // Per head: the sum over the 4 quarters (m is already common to
+        // them), then the wave's O^T, m and l to LDS.  Accumulator i holds,
+        // in lane (g4, n), rows r = 4 g4 + k of O^T for head n: dim
+        // 32 (i / 2) + 2 r + i % 2 (bf16) or 16 i + r (fp32).
+        l = xrow<16, false>(l);
+        l = xrow<32, false>(l);
+        if (n < G) {
 #pragma unroll
-                 for (int c = 0; c < CH; ++c)
-                     o[H][c] = rows_reduce<LPT, false>(o[H][c] * f);
-             }()),
-             ...);
-        }(std::make_integer_sequence<int, G>{});
-
-        if (r == 0) {
+            for (int i = 0; i < NACC; ++i)
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int c = 0; c < CH; ++c)
-                    lds_o[w][h * D + li * CH + c] = o[h][c];
-            if (li == 0) {
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    lds_m[w][h] = mw[h];
-                    lds_l[w][h] = lw[h];
+                for (int k = 0; k < 4; ++k) {
+                    const int r = 4 * g4 + k;
+                    const int d = DT == PKV_F32 ? 16 * i + r : 32 * (i >> 1) + 2 * r + (i & 1);
+                    lds_o[w][n * OSTR + d] = o[i][k];
                 }
+            if (g4 == 0) {
+                lds_m[w][n] = m;
+                lds_l[w][n] = l;
             }
         }
         __syncthreads();
@@ -664,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
                     const float ms = lds_m[s2][h];
                     const float f = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
                     Ls = __builtin_fmaf(lds_l[s2][h], f, Ls);
-                    O = __builtin_fmaf(lds_o[s2][idx], f, O);
+                    O = __builtin_fmaf(lds_o[s2][h * OSTR + d], f, O);
                 }
             }
             if (whole) {
@@ -708,14 +658,11 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
         // visits it, so its new row is written here.
         if (a.k_new && h == 0 && d < 2 * a.row_chunks) {
             const int nslot = a.slots[b];
-            const int bsz = a.stride > 0 ? a.block_size : 1;
-            if ((unsigned)nslot < (unsigned)(a.num_blocks * bsz)) {
+            if ((unsigned)nslot < (unsigned)(a.num_blocks * a.block_size)) {
                 const int kv = d / a.row_chunks, i = d % a.row_chunks;
                 const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
                     [((int64_t)b * a.Hkv + g) * a.row_chunks + i];
-                const int64_t dst = (((int64_t)(nslot / bsz) * a.Hkv + g) * bsz + nslot % bsz) *
-                                        a.row_chunks + i;
-                static_cast<uint4 *>(kv ? a.vc_w : a.kc_w)[dst] = row;
+                store_new_chunk(a, nslot, g, kv, i, row);
             }
         }
         return;
@@ -835,6 +782,7 @@ int launch_decode(const DecodeLaunch &d)
         a.vc_w = d.v_cache_w;
         a.row_chunks = d.head_dim * esz / 16;
         a.block_size = d.block_size;
+        a.head_dim = d.head_dim;
         a.stride = d.table_stride;
         a.B = nb;
         a.Hq = d.num_q_heads;

@@ -14,9 +14,11 @@
 // tile staged once serves all G heads of the group):
 //   * 4 waves x 32 rows.  Keys are processed in tiles of 64.  The workgroup
 //     stages each tile of K ([64][D], row-major) and V (transposed, [D][64],
-//     keys in the MFMA k order) into LDS from the paged cache with 16-byte
-//     loads, double buffered: the next tile's global loads are in flight
-//     while the current tile is computed.
+//     keys in the MFMA k order) into LDS from the paged cache with coalesced
+//     16-byte loads (1 KiB runs of a block's tile; the cache's V tiles
+//     already hold 4 consecutive keys of a dim together), double buffered:
+//     the next tile's global loads are in flight while the current tile is
+//     computed.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's
 //     Q rows held in registers for the whole kernel).  Computing the
 //     transpose leaves each lane with 4 consecutive keys of one query column,
@@ -97,19 +99,6 @@ __device__ __forceinline__ int vcol(int d, int pos)
 __device__ __forceinline__ int vpos(int kk)
 {
     return (kk & 32) | ((kk >> 2) & 3) << 3 | ((kk >> 4) & 1) << 2 | (kk & 3);
-}
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b)
-{
-    return (a & 0xFFFFu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b)
-{
-    return (a >> 16) | (b & 0xFFFF0000u);
-}
-__device__ __forceinline__ uint32_t word(const uint4 &v, int i)
-{
-    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f)
@@ -244,12 +233,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     };
 
     uint4 kst[Sh::KLD], vst[VK];
-    // Global loads of key tile kt into registers.  With this thread mapping
-    // every load of a wave falls in one block (the block index is
-    // wave-uniform for all supported shapes), so each load goes through a
-    // buffer resource on that block's (block, head) tile held in scalar
-    // registers; a block id outside the pool, or a block past the context,
-    // gets an empty resource and reads zeros without touching memory.
+    // Global loads of key tile kt into registers.  Wave w reads part wp of
+    // block w / WPB of the tile (WPB = waves per block), one 1 KiB run of the
+    // block's (block, head) tile per load: K keeps each token's dims in
+    // 16-byte chunks (chunk c of token t at (c * BS + t) * 16 bytes), V
+    // keeps 4 consecutive tokens of one dim together (element (t, d) at
+    // ((t / 4) * D + d) * 4 + t % 4).  Each load goes through a buffer
+    // resource on the wave's block held in scalar registers; a block id
+    // outside the pool, or a block past the context, gets an empty resource
+    // and reads zeros without touching memory.
+    constexpr int WPB = NW * BS / KT;                // waves per block of the tile
+    const int wblk = BS * (w / WPB);                 // the wave's first key in the tile
+    const int wp = w % WPB;
     auto tile_rsrc = [&](const uint16_t *base, int j) {
         const int jj = __builtin_amdgcn_readfirstlane(j);
         const int id = jj < L ? lds_ids[(jj / BS) % IDS] : -1;
@@ -260,61 +255,52 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
             ok ? (int)(hstride * 2) : 0, kRsrcWord3);
     };
     auto load_tile = [&](int kt) {
+        const auto rk = tile_rsrc(kg, kt * KT + wblk);
 #pragma unroll
-        for (int i = 0; i < Sh::KLD; ++i) {
-            const int cidx = tid + kThreads * i;
-            const int kk = cidx / CPR, cc = cidx % CPR;
-            const int j = kt * KT + kk;
-            // Keys past the context inside the last block read as the
-            // block's unused slots; they are masked before use.
+        for (int i = 0; i < Sh::KLD; ++i)
             kst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                tile_rsrc(kg, kt * KT + (w * 64) / CPR + (kThreads / CPR) * i),
-                ((j % BS) * D + cc * 8) * 2, 0, 0));
-        }
-        const int cc = tid % CPR, k0 = (tid / CPR) * VK;
+                rk, ((wp * Sh::KLD + i) * 64 + lane) * 16, 0, 0));
+        const auto rv = tile_rsrc(vg, kt * KT + wblk);
 #pragma unroll
-        for (int e = 0; e < VK; ++e) {
-            const int j = kt * KT + k0 + e;
+        for (int e = 0; e < VK; ++e)
             vst[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                tile_rsrc(vg, kt * KT + ((w * 64) / CPR) * VK), ((j % BS) * D + cc * 8) * 2, 0,
-                0));
-        }
+                rv, ((wp * VK + e) * 64 + lane) * 16, 0, 0));
         // Unused slots past the context end must not reach the PV product as
         // NaN (0 * NaN = NaN): zero them (only the tile holding the end).
         if (kt * KT + KT > L) {
 #pragma unroll
-            for (int e = 0; e < VK; ++e)
-                if (kt * KT + k0 + e >= L)
-                    vst[e] = make_uint4(0, 0, 0, 0);
+            for (int e = 0; e < VK; ++e) {
+                const int q = (wp * VK + e) * 64 + lane;     // 16-byte unit of the V tile
+                const int nv = L - (kt * KT + wblk + 4 * ((2 * q) / D));
+                const uint32_t m01 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+                const uint32_t m23 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+                vst[e].x &= m01;
+                vst[e].y &= m23;
+                vst[e].z &= m01;
+                vst[e].w &= m23;
+            }
         }
     };
-    // Registers -> LDS buffer: K as is, V transposed with its keys placed in
-    // MFMA k order.
+    // Registers -> LDS buffer: K rows as they are, V transposed with its
+    // keys placed in MFMA k order.  16-byte unit q of the wave's K part is
+    // chunk q / BS of token q % BS; unit q of its V part holds tokens
+    // 4 (2q / D) .. + 3 of dims 2 (q % (D / 2)) and the next.
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < Sh::KLD; ++i) {
-            const int cidx = tid + kThreads * i;
-            const int kk = cidx / CPR, cc = cidx % CPR;
+            const int q = (wp * Sh::KLD + i) * 64 + lane;
+            const int kk = wblk + q % BS, cc = q / BS;
             *reinterpret_cast<uint4 *>(&lds_k[buf][kk * KSTR + cc * 8]) = kst[i];
         }
-        const int cc = tid % CPR, k0 = (tid / CPR) * VK;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = cc * 8 + e;
-            uint16_t *vt = &lds_v[buf][d * VSTR + vcol(d, vpos(k0))];
-            const int wi = e >> 1;
-            if constexpr (VK == 4) {
-                uint2 pr;
-                pr.x = (e & 1) ? hi_pair(word(vst[0], wi), word(vst[1], wi))
-                               : lo_pair(word(vst[0], wi), word(vst[1], wi));
-                pr.y = (e & 1) ? hi_pair(word(vst[2], wi), word(vst[3], wi))
-                               : lo_pair(word(vst[2], wi), word(vst[3], wi));
-                *reinterpret_cast<uint2 *>(vt) = pr;
-            } else {
-                *reinterpret_cast<uint32_t *>(vt) =
-                    (e & 1) ? hi_pair(word(vst[0], wi), word(vst[1], wi))
-                            : lo_pair(word(vst[0], wi), word(vst[1], wi));
-            }
+        for (int e = 0; e < VK; ++e) {
+            const int q = (wp * VK + e) * 64 + lane;
+            const int k0 = wblk + 4 * ((2 * q) / D);
+            const int d0 = 2 * (q % (D / 2));
+            *reinterpret_cast<uint2 *>(&lds_v[buf][d0 * VSTR + vcol(d0, vpos(k0))]) =
+                make_uint2(vst[e].x, vst[e].y);
+            *reinterpret_cast<uint2 *>(&lds_v[buf][(d0 + 1) * VSTR + vcol(d0 + 1, vpos(k0))]) =
+                make_uint2(vst[e].z, vst[e].w);
         }
     };
 

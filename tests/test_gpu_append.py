@@ -25,6 +25,15 @@ def _image(cache):
     return kc, vc
 
 
+def _row(img: np.ndarray, blk: int, head: int, t: int, which: int) -> np.ndarray:
+    """Row of token offset t in tile (blk, head) of a cache image
+    [num_blocks][Hkv][bs][D], through the oracle's tile layout."""
+    _, _, bs, D = img.shape
+    flat = img[blk, head].reshape(-1)
+    return np.array([flat[oracle.tile_index(t, d, bs, D, img.dtype.itemsize)[which]]
+                     for d in range(D)], dtype=img.dtype)
+
+
 def _raw(rows, dtype):
     return rows.view(np.int32) if dtype == "f32" else rows.view(np.int16)
 
@@ -92,8 +101,10 @@ def test_append_is_idempotent_and_overwrites():
     cache.write(s, k2, k2)
     torch.cuda.synchronize()
     kc = cache.k_cache.cpu().numpy()
+    vc = cache.v_cache.cpu().numpy()
     for i, slot in enumerate(s):
-        assert np.array_equal(kc[slot // 16, 0, slot % 16], k2[i, 0])
+        assert np.array_equal(_row(kc, slot // 16, 0, slot % 16, 0), k2[i, 0])
+        assert np.array_equal(_row(vc, slot // 16, 0, slot % 16, 1), k2[i, 0])
 
 
 def test_logical_readback_after_appends_is_the_concatenation():
@@ -110,7 +121,12 @@ def test_logical_readback_after_appends_is_the_concatenation():
                 cache.extend(s, b.k[st[s] + t:st[s] + t + 1], b.v[st[s] + t:st[s] + t + 1])
     torch.cuda.synchronize()
     kc = cache.k_cache.view(torch.int16).cpu().numpy()
+    vc = cache.v_cache.view(torch.int16).cpu().numpy()
     for s in range(b.B):
         ids = cache.seqs.block_ids(s)
-        rows = np.concatenate([kc[i, :, :, :].transpose(1, 0, 2) for i in ids])[:b.lens[s]]
-        assert np.array_equal(rows, b.k[st[s]:st[s + 1]].view(np.int16))
+        for t in range(int(b.lens[s])):
+            for h in range(2):
+                assert np.array_equal(_row(kc, ids[t // 16], h, t % 16, 0),
+                                      b.k[st[s] + t, h].view(np.int16))
+                assert np.array_equal(_row(vc, ids[t // 16], h, t % 16, 1),
+                                      b.v[st[s] + t, h].view(np.int16))
