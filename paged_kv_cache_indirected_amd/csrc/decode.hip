@@ -637,12 +637,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
 
 // Log-sum-exp merge of the pieces of every (sequence, query head) cut
 // between workgroups: M = max_p m_p, L = sum_p l_p 2^(m_p - M),
-// out = sum_p o_p 2^(m_p - M) / L, summed in workgroup order over the
+// out = sum_p o_p 2^(m_p - M) / L, taken in workgroup order over the
 // workgroups whose ranges hold blocks of the sequence.  One workgroup per
 // (sequence, query head), one thread per output element; the pieces of a
-// sequence are consecutive in the workspace, and the loop over them is
-// unrolled so their loads are in flight together.  Empty sequences get zeros
-// here; sequences held whole by one workgroup were written by it.
+// sequence are consecutive in the workspace and are loaded in batches whose
+// loads are in flight together.  Empty sequences get zeros here; sequences
+// held whole by one workgroup were written by it.
 template <int D>
 __global__ __launch_bounds__(D) void k_merge(Args a)
 {
@@ -671,25 +671,38 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
     if (wf == wl)
         return;
     const bool sparse = T < a.W;   // only then can a range be empty
-    // Piece (w + b) of KV head g, query head h within the group.
+    // Piece (w + b) of KV head g, query head h within the group.  Pieces
+    // are read 8 at a time, all loads of a batch in flight together, and
+    // folded into a running (M, L, O) in workgroup order.
     const int64_t p0 = ((int64_t)g * (a.W + a.B) + b) * G + h;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int w = wf; w <= wl; ++w)
-        if (!sparse || !empty_range(w, T, a.W))
-            M = fmaxf(M, a.ws_ml[(p0 + (int64_t)w * G) * 2]);
-    float Ls = 0.0f, O = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-        for (int w = wf; w <= wl; ++w) {
-            if (sparse && empty_range(w, T, a.W))
-                continue;
+    float M = -INFINITY, Ls = 0.0f, O = 0.0f;
+    for (int w0 = wf; w0 <= wl; w0 += 8) {
+        float mp[8], lp[8], op[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int w = w0 + k;
+            const bool use = w <= wl && !(sparse && empty_range(w, T, a.W));
             const int64_t pr = p0 + (int64_t)w * G;
-            const float mp = a.ws_ml[pr * 2];
-            const float f = (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
-            Ls = __builtin_fmaf(a.ws_ml[pr * 2 + 1], f, Ls);
-            O = __builtin_fmaf(a.ws_o[pr * D + d], f, O);
+            mp[k] = use ? a.ws_ml[pr * 2] : -INFINITY;
+            lp[k] = use ? a.ws_ml[pr * 2 + 1] : 0.0f;
+            op[k] = use ? a.ws_o[pr * D + d] : 0.0f;
         }
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            Mn = fmaxf(Mn, mp[k]);
+        if (Mn != -INFINITY) {
+            const float f0 = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+            Ls *= f0;
+            O *= f0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float f = (mp[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp[k] - Mn);
+                Ls = __builtin_fmaf(lp[k], f, Ls);
+                O = __builtin_fmaf(op[k], f, O);
+            }
+        }
+        M = Mn;
     }
     store_out(a.out, a.out_dtype, oidx, Ls > 0.0f ? O / Ls : 0.0f);
 }
