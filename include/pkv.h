@@ -309,7 +309,35 @@ int pkv_seqs_append_batch_cow(pkv_seqs *seqs, int32_t n, const int64_t *seq_ids,
  * registered earlier under other contents is re-registered. */
 int32_t pkv_seqs_add_cached(pkv_seqs *seqs, int64_t seq_id, const int32_t *tokens, int32_t n);
 int pkv_seqs_cache(pkv_seqs *seqs, int64_t seq_id, const int32_t *tokens, int32_t n);
-/* Remove a sequence and drop its block references at once. */
+/* Swap ([KV-prep] "The KV cache": running out of KV memory stalls new
+ * requests or forces preemption of running ones; this is the preemption that
+ * keeps the KV instead of recomputing it).  `host` is a second pool whose ids
+ * name blocks of a host-side cache of the same block shape (e.g. pinned host
+ * memory); it must outlive the sequences swapped into it.
+ *
+ * pkv_seqs_swap_out: the blocks the sequence holds alone (refcount 1) get a
+ * host slot each and their device blocks return to the device pool; shared
+ * blocks stay resident and referenced.  Pair k is (dev_ids[k], host_ids[k]),
+ * *n pairs (cap >= the sequence's block count always suffices).  The caller
+ * copies those blocks device -> host (pkv_copy_blocks) on the stream before
+ * any later work that may write the freed device blocks.  All-or-nothing:
+ * PKV_ENOBLOCKS if the host pool is short.
+ * pkv_seqs_swap_in: fresh device blocks for the swapped blocks, pairs
+ * (host_ids[k], dev_ids[k]) to copy host -> device, host slots released.
+ * All-or-nothing: PKV_ENOBLOCKS if the device pool is short.
+ * While swapped out a sequence can only be swapped in, released, queried for
+ * its length or block list (host slots in place of the moved blocks) and
+ * counted; every other call on it returns PKV_ESTATE.  Recompute-style
+ * preemption needs no call of its own: release the sequence and admit it
+ * again later (pkv_seqs_add_cached reuses whatever stayed cached). */
+int pkv_seqs_swap_out(pkv_seqs *seqs, int64_t seq_id, pkv_pool *host, int32_t cap,
+                      int32_t *dev_ids, int32_t *host_ids, int32_t *n);
+int pkv_seqs_swap_in(pkv_seqs *seqs, int64_t seq_id, int32_t cap, int32_t *host_ids,
+                     int32_t *dev_ids, int32_t *n);
+/* 1 if swapped out, 0 if resident, -1 if unknown. */
+int pkv_seqs_is_swapped(const pkv_seqs *seqs, int64_t seq_id);
+/* Remove a sequence and drop its block references at once (host slots of a
+ * swapped-out sequence return to its host pool). */
 int pkv_seqs_release(pkv_seqs *seqs, int64_t seq_id);
 /* Length of a sequence, or -1 if unknown. */
 int32_t pkv_seqs_len(const pkv_seqs *seqs, int64_t seq_id);

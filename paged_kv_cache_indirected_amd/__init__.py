@@ -95,6 +95,9 @@ _sig("pkv_seqs_append_cow", ctypes.c_int, _P, _i64, _i32, _P, _P, _P, _P)
 _sig("pkv_seqs_append_batch_cow", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _P)
 _sig("pkv_seqs_add_cached", _i32, _P, _i64, _P, _i32)
 _sig("pkv_seqs_cache", ctypes.c_int, _P, _i64, _P, _i32)
+_sig("pkv_seqs_swap_out", ctypes.c_int, _P, _i64, _P, _i32, _P, _P, _P)
+_sig("pkv_seqs_swap_in", ctypes.c_int, _P, _i64, _i32, _P, _P, _P)
+_sig("pkv_seqs_is_swapped", ctypes.c_int, _P, _i64)
 _sig("pkv_seqs_release", ctypes.c_int, _P, _i64)
 _sig("pkv_seqs_len", _i32, _P, _i64)
 _sig("pkv_seqs_block_ids", _i32, _P, _i64, _i32, _P)
@@ -467,6 +470,39 @@ class Seqs:
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         _check(_lib.pkv_seqs_cache(self._h, int(seq_id), t.ctypes.data if len(t) else None,
                                    len(t)), "pkv_seqs_cache")
+
+    def swap_out(self, seq_id: int, host: Pool):
+        """Move the blocks the sequence holds alone to slots of ``host``;
+        returns the (device_block, host_slot) pairs to copy."""
+        import numpy as np
+        cap = max(len(self.block_ids(seq_id)), 1)
+        dev = np.empty(cap, dtype=np.int32)
+        hst = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(_lib.pkv_seqs_swap_out(self._h, int(seq_id), host.handle, cap, dev.ctypes.data,
+                                      hst.ctypes.data, ctypes.byref(n)), "pkv_seqs_swap_out")
+        # The host pool must outlive the swapped sequences: keep it referenced.
+        self._host_pools = getattr(self, "_host_pools", {})
+        self._host_pools[id(host)] = host
+        return list(zip(dev[:n.value].tolist(), hst[:n.value].tolist()))
+
+    def swap_in(self, seq_id: int):
+        """Bring a swapped sequence back; returns the (host_slot,
+        device_block) pairs to copy."""
+        import numpy as np
+        cap = max(len(self.block_ids(seq_id)), 1)
+        dev = np.empty(cap, dtype=np.int32)
+        hst = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(_lib.pkv_seqs_swap_in(self._h, int(seq_id), cap, hst.ctypes.data, dev.ctypes.data,
+                                     ctypes.byref(n)), "pkv_seqs_swap_in")
+        return list(zip(hst[:n.value].tolist(), dev[:n.value].tolist()))
+
+    def is_swapped(self, seq_id: int) -> bool:
+        r = int(_lib.pkv_seqs_is_swapped(self._h, int(seq_id)))
+        if r < 0:
+            raise PkvError(ESTATE, "pkv_seqs_is_swapped")
+        return bool(r)
 
     def release(self, seq_id: int) -> None:
         _check(_lib.pkv_seqs_release(self._h, int(seq_id)), "pkv_seqs_release")

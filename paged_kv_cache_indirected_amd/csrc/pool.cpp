@@ -290,6 +290,11 @@ namespace {
 struct Seq {
     int32_t len = 0;
     std::vector<int32_t> blocks;
+    // Swapped out: on_host[i] says blocks[i] is a slot of the host pool
+    // `host` (blocks the sequence held alone); shared blocks stay resident.
+    std::vector<char> on_host;
+    pkv_pool *host = nullptr;
+    bool swapped() const { return host != nullptr; }
 };
 }  // namespace
 
@@ -332,6 +337,8 @@ extern "C" int pkv_seqs_add_shared(pkv_seqs *s, int64_t id, int64_t src, int32_t
     auto it = s->seqs.find(src);
     if (it == s->seqs.end())
         return fail(PKV_ESTATE, "pkv_seqs_add_shared: unknown source %lld", (long long)src);
+    if (it->second.swapped())
+        return fail(PKV_ESTATE, "pkv_seqs_add_shared: source %lld is swapped out", (long long)src);
     if (s->seqs.count(id))
         return fail(PKV_ESTATE, "pkv_seqs_add_shared: sequence %lld exists", (long long)id);
     if (num_tokens < 0 || num_tokens % s->bs != 0 || num_tokens > it->second.len)
@@ -356,6 +363,8 @@ extern "C" int pkv_seqs_fork(pkv_seqs *s, int64_t id, int64_t src)
     auto it = s->seqs.find(src);
     if (it == s->seqs.end())
         return fail(PKV_ESTATE, "pkv_seqs_fork: unknown source %lld", (long long)src);
+    if (it->second.swapped())
+        return fail(PKV_ESTATE, "pkv_seqs_fork: source %lld is swapped out", (long long)src);
     if (s->seqs.count(id))
         return fail(PKV_ESTATE, "pkv_seqs_fork: sequence %lld exists", (long long)id);
     Seq n = it->second;
@@ -391,6 +400,8 @@ extern "C" int pkv_seqs_cache(pkv_seqs *s, int64_t id, const int32_t *tokens, in
     auto it = s->seqs.find(id);
     if (it == s->seqs.end())
         return fail(PKV_ESTATE, "pkv_seqs_cache: unknown sequence %lld", (long long)id);
+    if (it->second.swapped())
+        return fail(PKV_ESTATE, "pkv_seqs_cache: sequence %lld is swapped out", (long long)id);
     if (n > it->second.len)
         return fail(PKV_EINVAL, "pkv_seqs_cache: %d tokens given for a %d-token sequence", n,
                     it->second.len);
@@ -435,6 +446,8 @@ extern "C" int pkv_seqs_append(pkv_seqs *s, int64_t id, int32_t n, int32_t *slot
     if (it == s->seqs.end())
         return fail(PKV_ESTATE, "pkv_seqs_append: unknown sequence %lld", (long long)id);
     Seq &q = it->second;
+    if (q.swapped())
+        return fail(PKV_ESTATE, "pkv_seqs_append: sequence %lld is swapped out", (long long)id);
     if ((int64_t)q.len + n > INT32_MAX / 2)
         return fail(PKV_EINVAL, "pkv_seqs_append: sequence too long");
     if (writes_shared_block(s, q, n))
@@ -466,6 +479,9 @@ extern "C" int pkv_seqs_append_batch(pkv_seqs *s, int32_t n, const int64_t *ids,
                 return fail(PKV_EINVAL, "pkv_seqs_append_batch: sequence %lld listed twice",
                             (long long)ids[i]);
         qs[i] = &it->second;
+        if (qs[i]->swapped())
+            return fail(PKV_ESTATE, "pkv_seqs_append_batch: sequence %lld is swapped out",
+                        (long long)ids[i]);
         if (writes_shared_block(s, *qs[i], 1))
             return fail(PKV_ESTATE,
                         "pkv_seqs_append_batch: sequence %lld would write into a shared block",
@@ -510,6 +526,8 @@ extern "C" int pkv_seqs_append_cow(pkv_seqs *s, int64_t id, int32_t n, int32_t *
     if (it == s->seqs.end())
         return fail(PKV_ESTATE, "pkv_seqs_append_cow: unknown sequence %lld", (long long)id);
     Seq &q = it->second;
+    if (q.swapped())
+        return fail(PKV_ESTATE, "pkv_seqs_append_cow: sequence %lld is swapped out", (long long)id);
     if ((int64_t)q.len + n > INT32_MAX / 2)
         return fail(PKV_EINVAL, "pkv_seqs_append_cow: sequence too long");
     const bool cow = writes_shared_block(s, q, n);
@@ -547,6 +565,9 @@ extern "C" int pkv_seqs_append_batch_cow(pkv_seqs *s, int32_t n, const int64_t *
                 return fail(PKV_EINVAL, "pkv_seqs_append_batch_cow: sequence %lld listed twice",
                             (long long)ids[i]);
         qs[i] = &it->second;
+        if (qs[i]->swapped())
+            return fail(PKV_ESTATE, "pkv_seqs_append_batch_cow: sequence %lld is swapped out",
+                        (long long)ids[i]);
         if (writes_shared_block(s, *qs[i], 1))
             ++sharers[qs[i]->blocks.back()];
         total += blocks_needed(*qs[i], s->bs, 1);
@@ -580,11 +601,112 @@ extern "C" int pkv_seqs_release(pkv_seqs *s, int64_t id)
     auto it = s->seqs.find(id);
     if (it == s->seqs.end())
         return fail(PKV_ESTATE, "pkv_seqs_release: unknown sequence %lld", (long long)id);
-    int rc = pkv_pool_release(s->pool, (int32_t)it->second.blocks.size(), it->second.blocks.data());
-    if (rc != PKV_OK)
-        return rc;
+    Seq &q = it->second;
+    if (q.swapped()) {
+        std::vector<int32_t> dev, host;
+        for (size_t i = 0; i < q.blocks.size(); ++i)
+            (q.on_host[i] ? host : dev).push_back(q.blocks[i]);
+        int rc = pkv_pool_release(s->pool, (int32_t)dev.size(), dev.data());
+        if (rc != PKV_OK)
+            return rc;
+        rc = pkv_pool_release(q.host, (int32_t)host.size(), host.data());
+        if (rc != PKV_OK)
+            return rc;
+    } else {
+        int rc = pkv_pool_release(s->pool, (int32_t)q.blocks.size(), q.blocks.data());
+        if (rc != PKV_OK)
+            return rc;
+    }
     s->seqs.erase(it);
     return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Swap (preemption under KV pressure: "LLM Inference: KV Cache, Batching &
+// Scheduling", section "The KV cache", which warns that running out of KV
+// memory stalls new requests or forces preemption of running ones).
+
+extern "C" int pkv_seqs_swap_out(pkv_seqs *s, int64_t id, pkv_pool *host, int32_t cap,
+                                 int32_t *dev_ids, int32_t *host_ids, int32_t *n)
+{
+    if (!s || !host || host == s->pool || cap < 0 || !n || (cap > 0 && (!dev_ids || !host_ids)))
+        return fail(PKV_EINVAL, "pkv_seqs_swap_out: bad arguments");
+    auto it = s->seqs.find(id);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_swap_out: unknown sequence %lld", (long long)id);
+    Seq &q = it->second;
+    if (q.swapped())
+        return fail(PKV_ESTATE, "pkv_seqs_swap_out: sequence %lld is already swapped out",
+                    (long long)id);
+    // Blocks the sequence holds alone move; shared ones stay resident.
+    std::vector<size_t> mine;
+    for (size_t i = 0; i < q.blocks.size(); ++i)
+        if (pkv_pool_refcount(s->pool, q.blocks[i]) == 1)
+            mine.push_back(i);
+    if ((int64_t)mine.size() > cap)
+        return fail(PKV_EINVAL, "pkv_seqs_swap_out: %zu blocks move, room for %d", mine.size(),
+                    cap);
+    std::vector<int32_t> slots(mine.size());
+    int rc = pkv_pool_alloc(host, (int32_t)slots.size(), slots.data());
+    if (rc != PKV_OK)
+        return rc;
+    std::vector<int32_t> freed(mine.size());
+    q.on_host.assign(q.blocks.size(), 0);
+    for (size_t k = 0; k < mine.size(); ++k) {
+        const size_t i = mine[k];
+        dev_ids[k] = freed[k] = q.blocks[i];
+        host_ids[k] = slots[k];
+        q.blocks[i] = slots[k];
+        q.on_host[i] = 1;
+    }
+    q.host = host;
+    pkv_pool_release(s->pool, (int32_t)freed.size(), freed.data());
+    *n = (int32_t)mine.size();
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_swap_in(pkv_seqs *s, int64_t id, int32_t cap, int32_t *host_ids,
+                                int32_t *dev_ids, int32_t *n)
+{
+    if (!s || cap < 0 || !n || (cap > 0 && (!dev_ids || !host_ids)))
+        return fail(PKV_EINVAL, "pkv_seqs_swap_in: bad arguments");
+    auto it = s->seqs.find(id);
+    if (it == s->seqs.end())
+        return fail(PKV_ESTATE, "pkv_seqs_swap_in: unknown sequence %lld", (long long)id);
+    Seq &q = it->second;
+    if (!q.swapped())
+        return fail(PKV_ESTATE, "pkv_seqs_swap_in: sequence %lld is resident", (long long)id);
+    std::vector<size_t> away;
+    for (size_t i = 0; i < q.blocks.size(); ++i)
+        if (q.on_host[i])
+            away.push_back(i);
+    if ((int64_t)away.size() > cap)
+        return fail(PKV_EINVAL, "pkv_seqs_swap_in: %zu blocks move, room for %d", away.size(),
+                    cap);
+    std::vector<int32_t> fresh(away.size());
+    int rc = pkv_pool_alloc(s->pool, (int32_t)fresh.size(), fresh.data());
+    if (rc != PKV_OK)
+        return rc;
+    std::vector<int32_t> slots(away.size());
+    for (size_t k = 0; k < away.size(); ++k) {
+        const size_t i = away[k];
+        host_ids[k] = slots[k] = q.blocks[i];
+        dev_ids[k] = fresh[k];
+        q.blocks[i] = fresh[k];
+    }
+    pkv_pool_release(q.host, (int32_t)slots.size(), slots.data());
+    q.host = nullptr;
+    q.on_host.clear();
+    *n = (int32_t)away.size();
+    return PKV_OK;
+}
+
+extern "C" int pkv_seqs_is_swapped(const pkv_seqs *s, int64_t id)
+{
+    if (!s)
+        return -1;
+    auto it = s->seqs.find(id);
+    return it == s->seqs.end() ? -1 : (it->second.swapped() ? 1 : 0);
 }
 
 extern "C" int32_t pkv_seqs_len(const pkv_seqs *s, int64_t id)
@@ -618,6 +740,9 @@ extern "C" int pkv_seqs_fill(const pkv_seqs *s, int32_t n, const int64_t *ids, i
         auto it = s->seqs.find(ids[i]);
         if (it == s->seqs.end())
             return fail(PKV_ESTATE, "pkv_seqs_fill: unknown sequence %lld", (long long)ids[i]);
+        if (it->second.swapped())
+            return fail(PKV_ESTATE, "pkv_seqs_fill: sequence %lld is swapped out",
+                        (long long)ids[i]);
         if ((int64_t)it->second.blocks.size() > stride)
             return fail(PKV_EINVAL, "pkv_seqs_fill: sequence %lld has %zu blocks > stride %d",
                         (long long)ids[i], it->second.blocks.size(), stride);

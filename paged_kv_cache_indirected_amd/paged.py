@@ -17,7 +17,7 @@ from typing import Iterable, Optional
 import numpy as np
 import torch
 
-from . import BF16, F32, CacheDesc, Pool, Seqs, append, copy_blocks
+from . import BF16, F32, CacheDesc, Pool, Seqs, append, copy_blocks  # noqa: F401
 
 # Quiet-NaN bit patterns written into every cache element before any append,
 # so a read of an unused slot or block would surface in the output.
@@ -119,6 +119,39 @@ class PagedCache:
         self.copy(copies)
         self.write(slots, k_rows, v_rows)
         return slots, copies
+
+    def attach_swap(self, num_blocks: int) -> None:
+        """A pinned-host swap area of num_blocks blocks (same block shape)
+        with its own pool of slots."""
+        d = self.desc
+        self.swap_desc = CacheDesc(int(num_blocks), d.num_kv_heads, d.block_size, d.head_dim,
+                                   d.dtype)
+        shape = self.swap_desc.cache_shape()
+        self.swap_k = torch.zeros(shape, dtype=torch_dtype(d.dtype)).pin_memory()
+        self.swap_v = torch.zeros(shape, dtype=torch_dtype(d.dtype)).pin_memory()
+        self.swap_pool = Pool(int(num_blocks), 0)
+
+    def _copy_pairs(self, pairs, to_host: bool) -> None:
+        if not pairs:
+            return
+        ids = torch.tensor(np.asarray(pairs, dtype=np.int32).T.copy(), device=self.device)
+        if to_host:
+            copy_blocks(self.k_cache, self.v_cache, self.desc, self.swap_k, self.swap_v,
+                        self.swap_desc, ids[0].contiguous(), ids[1].contiguous())
+        else:
+            copy_blocks(self.swap_k, self.swap_v, self.swap_desc, self.k_cache, self.v_cache,
+                        self.desc, ids[0].contiguous(), ids[1].contiguous())
+
+    def swap_out(self, seq_id: int):
+        """Preempt a sequence by moving its private blocks to the swap area."""
+        pairs = self.seqs.swap_out(int(seq_id), self.swap_pool)
+        self._copy_pairs(pairs, to_host=True)
+        return pairs
+
+    def swap_in(self, seq_id: int):
+        pairs = self.seqs.swap_in(int(seq_id))
+        self._copy_pairs(pairs, to_host=False)
+        return pairs
 
     def admit_cached(self, seq_id: int, tokens) -> int:
         """New sequence for a prompt, reusing cached prefix blocks; returns

@@ -212,3 +212,33 @@ def test_prefix_cache_reuse_prefill_matches_oracle():
     assert cache.pool.num_cached == (len(tok_a) // bs) + (len(tok_b) // bs) - P // bs
     expect = oracle.reusable_prefix_tokens(list(tok_b), [list(tok_a), list(tok_b)], bs)
     assert cache.admit_cached(2, tok_b) == expect == (len(tok_b) - 1) // bs * bs
+
+
+# --------------------------------------------------------------------------
+# Preemption by swap, end to end: swap out, let other work overwrite every
+# free device block, swap back in, decode again.
+
+@pytest.mark.parametrize("dtype,D,bs", [("bf16", 128, 16), ("f32", 64, 32)])
+def test_swap_roundtrip_decode_bitwise(dtype, D, bs):
+    from harness import decode_state
+    b = synth.custom_decode(47, [40, 300, 17, 129, 1, 64], Hq=16, Hkv=2, D=D, dtype=dtype,
+                            block_size=bs)
+    say(f"[swap] {dtype} D={D} bs={bs} lens={list(b.lens)}")
+    cache, q, tab, lens, mx = decode_state(b)
+    before = run_decode(cache, q, tab, lens, mx, b.shape.scale)
+    cache.attach_swap(64)
+    moved = cache.swap_out(1) + cache.swap_out(3)
+    assert moved and cache.seqs.is_swapped(1)
+    # Another sequence takes every free device block and fills it with junk.
+    nfree = cache.pool.num_free
+    junk = synth.normal(synth.rng(47, 9), (nfree * bs, 2, D), dtype)
+    cache.seqs.add(99)
+    cache.extend(99, junk, junk)
+    cache.release(99)
+    cache.swap_in(1)
+    cache.swap_in(3)
+    tab2, lens2, mx2 = cache.tables(range(b.B))
+    after = run_decode(cache, q, tab2, lens2, mx2, b.shape.scale)
+    assert torch.equal(before, after)
+    ref = oracle.decode(b.q, b.k, b.v, b.lens, b.shape.scale)
+    assert max_err(after, ref) <= TOL[dtype]
