@@ -451,6 +451,92 @@ def bench_prefix_ttft(timer):
                     "figure is for a whole model"}
 
 
+def bench_sched(steps=300, warm=60):
+    """The token-budget step scheduler driving the kernels: synthetic
+    arrivals (Poisson, 0.25 requests per step; prompts U[512,4096], outputs
+    U[64,256]), Llama-70B-shaped heads, 16-token blocks.  Each step appends
+    the planned rows, runs pkv_prefill_chunk over the chunks and pkv_decode
+    over the decode tokens.  Chunked (budget 2048, 512-token chunks) and
+    unchunked (whole prompts, budget 4096 + decode) runs see the same
+    arrivals.  Per step: GPU time of its kernels (HIP events); per request:
+    TTFT = GPU time from the start of its arrival step to the end of the step
+    that completes its prompt."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    from paged_kv_cache_indirected_amd.paged import PagedCache
+    Hq, Hkv, D, bs = 64, 8, 128, 16
+    scale = 1.0 / np.sqrt(D)
+    g = np.random.default_rng(2024)
+    arrivals = g.poisson(0.25, size=steps)
+    lens = [(int(g.integers(512, 4097)), int(g.integers(64, 257))) for _ in range(int(arrivals.sum()))]
+    rows = torch.randn((8192, Hkv, D), device="cuda").to(torch.bfloat16)
+    qrows = torch.randn((8192, Hq, D), device="cuda").to(torch.bfloat16)
+    out = {}
+    for label, budget, chunk in (("chunked_512", 2048, 512), ("unchunked", 4096 + 64, 4096)):
+        cache = PagedCache(12288, Hkv, bs, D, pkv.BF16, pool_seed=7)
+        sc = pkv.Sched(cache.pool, cache.seqs, budget, chunk, max_running=64)
+        ws = torch.zeros(pkv.decode_workspace_bytes(64, Hq, 8192, cache.desc), dtype=torch.uint8,
+                         device="cuda")
+        pout = torch.empty((budget, Hq, D), dtype=torch.float32, device="cuda")
+        dout = torch.empty((64, Hq, D), dtype=torch.float32, device="cuda")
+        step_ms, arrive, ttft, clock, decoded, nreq = [], {}, [], 0.0, 0, 0
+        for st in range(steps):
+            for _ in range(int(arrivals[st])):
+                sc.submit(nreq, *lens[nreq])
+                arrive[nreq] = clock
+                nreq += 1
+            p = sc.step()
+            slots = np.concatenate([p["chunk_slots"], p["decode_slots"]]).astype(np.int32)
+            n = len(slots)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            if len(p["chunk_ids"]):
+                ptab, plens, pmx = cache.tables(list(p["chunk_ids"]))
+                qs = torch.from_numpy(np.concatenate([[0], np.cumsum(p["chunk_len"])])
+                                      .astype(np.int32)).cuda()
+            if len(p["decode_ids"]):
+                dtab, dlens, dmx = cache.tables(list(p["decode_ids"]))
+            sl = torch.from_numpy(slots).cuda()
+            e0.record()
+            if n:
+                pkv.append(rows[:n], rows[:n], sl, cache.k_cache, cache.v_cache, cache.desc)
+            if len(p["chunk_ids"]):
+                T = int(p["chunk_len"].sum())
+                pkv.prefill_chunk(qrows[:T], qs, cache.k_cache, cache.v_cache, ptab, plens, scale,
+                                  pout[:T], cache.desc, int(p["chunk_len"].max()), pmx)
+            if len(p["decode_ids"]):
+                B = len(p["decode_ids"])
+                pkv.decode(qrows[:B], cache.k_cache, cache.v_cache, dtab, dlens, scale, dout[:B],
+                           cache.desc, dmx, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            clock += ms
+            if st >= warm:
+                step_ms.append(ms)
+                decoded += len(p["decode_ids"])
+                for rid in p["first_ids"]:
+                    ttft.append(clock - arrive[int(rid)])
+        sm = np.array(step_ms)
+        tt = np.array(ttft) if ttft else np.zeros(1)
+        out[label] = {"token_budget": budget, "chunk_tokens": chunk,
+                      "step_ms_p50": round(float(np.percentile(sm, 50)), 3),
+                      "step_ms_p90": round(float(np.percentile(sm, 90)), 3),
+                      "step_ms_p99": round(float(np.percentile(sm, 99)), 3),
+                      "step_ms_max": round(float(sm.max()), 3),
+                      "ttft_ms_mean": round(float(tt.mean()), 3),
+                      "ttft_ms_p90": round(float(np.percentile(tt, 90)), 3),
+                      "first_tokens": len(ttft),
+                      "decode_tokens_per_s": round(decoded / (sm.sum() * 1e-3), 1),
+                      "running_at_end": sc.num_running, "waiting_at_end": sc.num_waiting}
+        del cache, sc
+        torch.cuda.empty_cache()
+    out["workload"] = ("step scheduler: Poisson 0.25 req/step, prompts U[512,4096], outputs "
+                       "U[64,256], 64q/8kv, d128, bf16, block 16, max 64 running; steps "
+                       f"{warm}..{steps} timed (GPU time of each step's kernels)")
+    return out
+
+
 def probe_copy(nbytes=1 << 30, reps=3):
     """Run only the plain copy probe (nbytes read + nbytes written per call),
     so that a hardware-counter run sees a kernel of known traffic."""
@@ -523,7 +609,7 @@ def main():
                     help="skip the other workloads and the probes")
     ap.add_argument("--only", choices=["continuous_batching", "prefix_sharing",
                                        "chunked_prefill_mixed", "block_copy",
-                                       "prefix_cache_ttft"],
+                                       "prefix_cache_ttft", "step_scheduler"],
                     help="run one secondary workload alone (for profiling) and print its JSON")
     ap.add_argument("--probe-copy", action="store_true",
                     help="run only the copy probe (for hardware-counter scaling)")
@@ -556,7 +642,8 @@ def main():
                "prefix_sharing": lambda: bench_cfg4(timer, args.splits),
                "chunked_prefill_mixed": lambda: bench_cfg5(timer, args.splits),
                "block_copy": lambda: bench_block_copy(timer),
-               "prefix_cache_ttft": lambda: bench_prefix_ttft(timer)}
+               "prefix_cache_ttft": lambda: bench_prefix_ttft(timer),
+               "step_scheduler": lambda: bench_sched()}
         print(json.dumps({args.only: fns[args.only]()}), flush=True)
         return
     batch = synth.cfg2()
@@ -688,6 +775,9 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] prefix cache TTFT proxy")
         wl["prefix_cache_ttft"] = bench_prefix_ttft(timer)
+        torch.cuda.empty_cache()
+        log("[bench] step scheduler")
+        wl["step_scheduler"] = bench_sched()
         res["workloads"] = wl
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")

@@ -351,6 +351,60 @@ int pkv_seqs_fill(const pkv_seqs *seqs, int32_t n, const int64_t *seq_ids,
                   int32_t *block_tables, int32_t stride, int32_t *context_lens);
 int pkv_seqs_stats_get(const pkv_seqs *seqs, pkv_seqs_stats *out);
 
+/* ------------------------------------------------------------------------
+ * Token-budget step scheduler ([KV-prep] "Continuous batching (Orca)":
+ * sequences join and leave every step; "Chunked prefill": prompts are split
+ * into fixed-size chunks, e.g. 512 tokens, that share steps with decode
+ * tokens; "The KV cache" warning: when KV memory runs out new requests stall
+ * or running ones are preempted).  The scheduler owns the sequences it
+ * creates in `seqs` (ids are the request ids); single-threaded.
+ *
+ * Each step, under token_budget tokens: finished sequences of the previous
+ * step are released; every running sequence whose prompt is complete gets
+ * one decode token (admission order); the rest of the budget goes to prefill
+ * chunks of at most chunk_tokens, first to running sequences still
+ * prefilling, then to queued requests admitted first come first served (at
+ * most max_running sequences run).  If the pool cannot hold the plan, queued
+ * requests stall; if running sequences alone do not fit, the most recently
+ * admitted is preempted by recompute (blocks released, back to the front of
+ * the queue with its progress reset).  The step's slots are allocated from
+ * the pool (pkv_seqs_append); the caller then appends the rows (pkv_append),
+ * runs pkv_prefill_chunk over the chunks and pkv_decode over the decode
+ * sequences, with block tables from pkv_seqs_fill.
+ *
+ * A request generates max_new_tokens tokens: the first when its prompt's
+ * last chunk is processed (listed in first_ids: the time-to-first-token
+ * event), then one per decode step.  It is listed in finished_ids in the
+ * step that produces its last token and released at the next step.
+ */
+typedef struct pkv_sched pkv_sched;
+
+typedef struct pkv_step_plan {
+    /* Caller-provided arrays: max_running entries each, except chunk_slots
+     * (token_budget entries). */
+    int64_t *decode_ids;      /* sequences with one decode token this step */
+    int32_t *decode_slots;    /* the slot of that token */
+    int64_t *chunk_ids;       /* sequences with a prefill chunk this step */
+    int32_t *chunk_prior;     /* prompt tokens already in the cache before the chunk */
+    int32_t *chunk_len;       /* chunk tokens */
+    int32_t *chunk_slots;     /* slots of all chunk tokens, chunk after chunk */
+    int64_t *first_ids;       /* prompt completed this step (first token) */
+    int64_t *finished_ids;    /* last token produced this step */
+    int64_t *preempted_ids;   /* preempted (recompute) while planning this step */
+    /* Counts written by pkv_sched_step. */
+    int32_t n_decode, n_chunks, n_chunk_tokens, n_first, n_finished, n_preempted;
+} pkv_step_plan;
+
+pkv_sched *pkv_sched_create(pkv_pool *pool, pkv_seqs *seqs, int32_t block_size,
+                            int32_t token_budget, int32_t chunk_tokens, int32_t max_running);
+void pkv_sched_destroy(pkv_sched *sched);
+/* Queue a request; PKV_ESTATE if the id is queued or is a sequence of seqs. */
+int pkv_sched_submit(pkv_sched *sched, int64_t req_id, int32_t prompt_len,
+                     int32_t max_new_tokens);
+int pkv_sched_step(pkv_sched *sched, pkv_step_plan *plan);
+int32_t pkv_sched_num_waiting(const pkv_sched *sched);
+int32_t pkv_sched_num_running(const pkv_sched *sched);
+
 #ifdef __cplusplus
 }
 #endif

@@ -105,6 +105,22 @@ _sig("pkv_seqs_fill", ctypes.c_int, _P, _i32, _P, _P, _i32, _P)
 _sig("pkv_seqs_stats_get", ctypes.c_int, _P, ctypes.POINTER(SeqsStatsC))
 
 
+class StepPlanC(ctypes.Structure):
+    _fields_ = [("decode_ids", _P), ("decode_slots", _P), ("chunk_ids", _P),
+                ("chunk_prior", _P), ("chunk_len", _P), ("chunk_slots", _P),
+                ("first_ids", _P), ("finished_ids", _P), ("preempted_ids", _P),
+                ("n_decode", _i32), ("n_chunks", _i32), ("n_chunk_tokens", _i32),
+                ("n_first", _i32), ("n_finished", _i32), ("n_preempted", _i32)]
+
+
+_sig("pkv_sched_create", _P, _P, _P, _i32, _i32, _i32, _i32)
+_sig("pkv_sched_destroy", None, _P)
+_sig("pkv_sched_submit", ctypes.c_int, _P, _i64, _i32, _i32)
+_sig("pkv_sched_step", ctypes.c_int, _P, ctypes.POINTER(StepPlanC))
+_sig("pkv_sched_num_waiting", _i32, _P)
+_sig("pkv_sched_num_running", _i32, _P)
+
+
 class PkvError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -532,3 +548,62 @@ class Seqs:
         st = SeqsStatsC()
         _check(_lib.pkv_seqs_stats_get(self._h, ctypes.byref(st)), "pkv_seqs_stats_get")
         return {f: getattr(st, f) for f, _ in SeqsStatsC._fields_}
+
+
+class Sched:
+    """pkv_sched_*: token-budget step scheduler over a Pool and Seqs."""
+
+    def __init__(self, pool: Pool, seqs: Seqs, token_budget: int, chunk_tokens: int,
+                 max_running: int):
+        import numpy as np
+        self.pool, self.seqs = pool, seqs   # keep them alive
+        self._h = _lib.pkv_sched_create(pool.handle, seqs._h, seqs.block_size, int(token_budget),
+                                        int(chunk_tokens), int(max_running))
+        if not self._h:
+            raise PkvError(EINVAL, "pkv_sched_create")
+        R, T = max(int(max_running), 1), max(int(token_budget), 1)
+        self._a = {
+            "decode_ids": np.empty(R, np.int64), "decode_slots": np.empty(R, np.int32),
+            "chunk_ids": np.empty(R, np.int64), "chunk_prior": np.empty(R, np.int32),
+            "chunk_len": np.empty(R, np.int32), "chunk_slots": np.empty(T, np.int32),
+            "first_ids": np.empty(R, np.int64), "finished_ids": np.empty(R, np.int64),
+            "preempted_ids": np.empty(R, np.int64),
+        }
+        self._plan = StepPlanC(*[self._a[f].ctypes.data for f, _ in StepPlanC._fields_[:9]])
+
+    def close(self) -> None:
+        if self._h and _lib is not None:
+            _lib.pkv_sched_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def submit(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
+        _check(_lib.pkv_sched_submit(self._h, int(req_id), int(prompt_len), int(max_new_tokens)),
+               "pkv_sched_submit")
+
+    def step(self) -> dict:
+        """Plan one step; returns copies of the plan's arrays."""
+        p = self._plan
+        _check(_lib.pkv_sched_step(self._h, ctypes.byref(p)), "pkv_sched_step")
+        a = self._a
+        return {
+            "decode_ids": a["decode_ids"][:p.n_decode].copy(),
+            "decode_slots": a["decode_slots"][:p.n_decode].copy(),
+            "chunk_ids": a["chunk_ids"][:p.n_chunks].copy(),
+            "chunk_prior": a["chunk_prior"][:p.n_chunks].copy(),
+            "chunk_len": a["chunk_len"][:p.n_chunks].copy(),
+            "chunk_slots": a["chunk_slots"][:p.n_chunk_tokens].copy(),
+            "first_ids": a["first_ids"][:p.n_first].copy(),
+            "finished_ids": a["finished_ids"][:p.n_finished].copy(),
+            "preempted_ids": a["preempted_ids"][:p.n_preempted].copy(),
+        }
+
+    @property
+    def num_waiting(self) -> int:
+        return int(_lib.pkv_sched_num_waiting(self._h))
+
+    @property
+    def num_running(self) -> int:
+        return int(_lib.pkv_sched_num_running(self._h))

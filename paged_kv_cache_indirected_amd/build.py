@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")   # measurement probes, loaded by the benchmark only
 OBJ = os.path.join(ROOT, "_build", "pkv")
 
-HOST_SRC = ["errors.cpp", "pool.cpp", "api.cpp"]
+HOST_SRC = ["errors.cpp", "pool.cpp", "sched.cpp", "api.cpp"]
 HIP_SRC = ["append.hip", "copy.hip", "decode.hip", "prefill.hip"]
 
 ARCH = "gfx950"
