@@ -180,6 +180,36 @@ int pkv_append_decode(const void *k_new, const void *v_new, const int32_t *slot_
                       size_t workspace_bytes, const pkv_cache_desc *c, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Cascade decode over a shared prefix ([KV-news] section 2 and [KV-blog]
+ * "The Elegant Fix": sequences with an identical prefix share its pages;
+ * [KV-prep] "Prefix caching").  Reading every shared block once per sharer
+ * is what plain decode does; here the shared prefix's blocks are read once
+ * for all sequences of the call.
+ *
+ * Sequence b attends prefix_len tokens held in prefix_blocks ([prefix_len /
+ * block_size] int32, device) followed by its own context_lens[b] tokens in
+ * block_tables[b] (which lists only its own blocks).  The result equals
+ * pkv_decode over the concatenated block lists, up to rounding order.
+ * prefix_len must be a whole number of blocks (0 allowed).  The prefix runs
+ * as a non-causal MFMA pass over all sequences' queries, split over ranges
+ * of prefix blocks; the suffixes as the split decode; the states are merged
+ * by log-sum-exp.  bf16 caches only (PKV_EUNSUPPORTED otherwise).  Other
+ * arguments as pkv_decode (max_context_len bounds context_lens); the
+ * workspace (size from pkv_decode_cascade_workspace_bytes) needs no
+ * initialisation, and calls sharing one must not overlap.
+ */
+size_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t prefix_len, int32_t max_context_len,
+                                          const pkv_cache_desc *c);
+int pkv_decode_cascade(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *prefix_blocks, int32_t prefix_len,
+                       const int32_t *block_tables, int32_t block_table_stride,
+                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+                       void *workspace, size_t workspace_bytes, const pkv_cache_desc *c,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
  * Causal chunked prefill ([KV-prep] "Chunked prefill": a prompt is split into
  * fixed-size chunks, e.g. 512 tokens, interleaved with decode; the split does
  * not change the result).

@@ -6,7 +6,8 @@ torch supplies device memory and streams.  There is no fallback: if the
 library is not built, importing this package fails.
 
 Calls mirror the C ABI names: ``append`` (pkv_append), ``decode``
-(pkv_decode), ``append_decode`` (pkv_append_decode), ``prefill_chunk``
+(pkv_decode), ``append_decode`` (pkv_append_decode), ``decode_cascade``
+(pkv_decode_cascade), ``prefill_chunk``
 (pkv_prefill_chunk), ``copy_blocks`` (pkv_copy_blocks), ``Pool``
 (pkv_pool_*) and ``Seqs`` (pkv_seqs_*).
 """
@@ -73,6 +74,9 @@ _sig("pkv_decode", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, cty
 _sig("pkv_append_decode", ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32,
      ctypes.c_float, _P, _i32, _i32, _P, _sz, _DESC, _P)
 _sig("pkv_prefill_workspace_bytes", _sz, _i32, _i32, _i32, _DESC)
+_sig("pkv_decode_cascade_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _DESC)
+_sig("pkv_decode_cascade", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _P, _i32, _i32, _i32,
+     ctypes.c_float, _P, _i32, _P, _sz, _DESC, _P)
 _sig("pkv_prefill_chunk", ctypes.c_int, _P, _P, _i32, _i32, _P, _P, _P, _i32, _P, _i32, _i32,
      ctypes.c_float, _P, _i32, _P, _sz, _DESC, _P)
 _sig("pkv_pool_create", _P, _i32, _u64)
@@ -307,6 +311,42 @@ def append_decode(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables,
                                 _dtype_code(out), int(num_splits), _dev(workspace, "workspace"),
                                 ws_bytes, ctypes.byref(desc.c()), _stream(stream))
     _check(rc, "pkv_append_decode")
+
+
+def decode_cascade_workspace_bytes(num_seqs: int, num_q_heads: int, prefix_len: int,
+                                   max_context_len: int, desc: CacheDesc) -> int:
+    return int(_lib.pkv_decode_cascade_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                                       int(prefix_len), int(max_context_len),
+                                                       ctypes.byref(desc.c())))
+
+
+def decode_cascade(q, k_cache, v_cache, prefix_blocks, prefix_len: int, block_tables,
+                   context_lens, scale: float, out, desc: CacheDesc,
+                   max_context_len: Optional[int] = None, workspace=None, stream=None) -> None:
+    """pkv_decode_cascade: decode over a shared prefix (prefix_blocks, int32
+    [prefix_len / block_size]) followed by each sequence's own blocks
+    (block_tables [B][stride], context_lens [B] = own tokens)."""
+    torch = _torch()
+    B, Hq, D = (int(x) for x in q.shape)
+    _need(D == desc.head_dim, "q head_dim does not match the descriptor")
+    _cache_ok(k_cache, desc, "k_cache")
+    _cache_ok(v_cache, desc, "v_cache")
+    _need(block_tables.dim() == 2 and int(block_tables.shape[0]) == B, "block_tables must be [B][stride]")
+    stride = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = stride * desc.block_size
+    nbytes = decode_cascade_workspace_bytes(B, Hq, prefix_len, max_context_len, desc)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    pb = _dev(prefix_blocks, "prefix_blocks", torch.int32) if prefix_len > 0 else None
+    rc = _lib.pkv_decode_cascade(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), pb, int(prefix_len),
+        _dev(block_tables, "block_tables", torch.int32), stride,
+        _dev(context_lens, "context_lens", torch.int32), B, Hq, int(max_context_len),
+        float(scale), _dev(out, "out"), _dtype_code(out), _dev(workspace, "workspace"),
+        int(workspace.numel() * workspace.element_size()), ctypes.byref(desc.c()),
+        _stream(stream))
+    _check(rc, "pkv_decode_cascade")
 
 
 def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, max_query_len: int,

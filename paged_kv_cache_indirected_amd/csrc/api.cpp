@@ -180,7 +180,7 @@ int decode_call(const char *who, const void *q, const void *k_cache, const void 
                 int32_t max_context_len, float scale, void *out, int32_t out_dtype,
                 int32_t num_splits, void *workspace, size_t workspace_bytes,
                 const pkv_cache_desc *c, void *stream, const void *k_new, const void *v_new,
-                const int32_t *slots)
+                const int32_t *slots, float *lse = nullptr)
 {
     int rc = check_desc(c, who);
     if (rc || (rc = check_heads(num_q_heads, c, who)))
@@ -250,7 +250,39 @@ int decode_call(const char *who, const void *q, const void *k_cache, const void 
     d.k_cache_w = const_cast<void *>(k_cache);
     d.v_cache_w = const_cast<void *>(v_cache);
     d.stream = stream;
+    d.lse = lse;
     return pkv::launch_decode(d);
+}
+
+// Cascade decode: prefix splits, then the suffix decode's own workspace.
+int32_t cascade_splits(int32_t B, int32_t hq, int32_t nb, const pkv_cache_desc *c)
+{
+    if (nb <= 0 || B <= 0)
+        return 0;
+    const int64_t tq = 128 / (hq / c->num_kv_heads);          // query tokens per prefill tile
+    const int64_t per = (int64_t)c->num_kv_heads * ((B + tq - 1) / tq);
+    int64_t ks = (pkv::device_cu_count() + per - 1) / per;
+    ks = ks < 1 ? 1 : (ks > nb ? nb : ks);
+    ks = ks > 4096 ? 4096 : ks;
+    const int64_t nbk = (nb + ks - 1) / ks;
+    return (int32_t)((nb + nbk - 1) / nbk);
+}
+
+struct CascadeWs {
+    size_t qs, lens, o, lse, dws, total;
+};
+
+CascadeWs cascade_layout(int32_t B, int32_t hq, int32_t D, int32_t ks, int32_t W)
+{
+    const size_t rows = (size_t)B * hq, states = (size_t)ks + 1;
+    CascadeWs l;
+    l.qs = 0;
+    l.lens = align256(((size_t)ks + 1) * sizeof(int32_t));
+    l.o = l.lens + align256(((size_t)ks + 1) * sizeof(int32_t));
+    l.lse = l.o + align256(states * rows * D * sizeof(float));
+    l.dws = l.lse + align256(states * rows * sizeof(float));
+    l.total = l.dws + ws_layout(B, hq, W, D).total;
+    return l;
 }
 
 }  // namespace
@@ -285,6 +317,92 @@ extern "C" int pkv_append_decode(const void *k_new, const void *v_new,
                        context_lens, num_seqs, num_q_heads, max_context_len, scale, out, out_dtype,
                        num_splits, workspace, workspace_bytes, c, stream, k_new, v_new,
                        slot_mapping);
+}
+
+extern "C" size_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                     int32_t prefix_len, int32_t max_context_len,
+                                                     const pkv_cache_desc *c)
+{
+    if (check_desc(c, "pkv_decode_cascade_workspace_bytes") || num_seqs <= 0 ||
+        check_heads(num_q_heads, c, "pkv_decode_cascade_workspace_bytes") || prefix_len < 0)
+        return 0;
+    const int32_t ks = cascade_splits(num_seqs, num_q_heads, prefix_len / c->block_size, c);
+    const int32_t W = auto_splits(num_seqs, max_context_len, c);
+    return cascade_layout(num_seqs, num_q_heads, c->head_dim, ks, W).total;
+}
+
+extern "C" int pkv_decode_cascade(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *prefix_blocks, int32_t prefix_len,
+                                  const int32_t *block_tables, int32_t block_table_stride,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len, float scale,
+                                  void *out, int32_t out_dtype, void *workspace,
+                                  size_t workspace_bytes, const pkv_cache_desc *c, void *stream)
+{
+    static const char *who = "pkv_decode_cascade";
+    pkv::clear_error();
+    int rc = check_desc(c, who);
+    if (rc || (rc = check_heads(num_q_heads, c, who)))
+        return rc;
+    if (c->dtype != PKV_BF16)
+        return fail(PKV_EUNSUPPORTED, "%s: bf16 caches only", who);
+    if (prefix_len < 0 || prefix_len % c->block_size != 0)
+        return fail(PKV_EINVAL, "%s: prefix_len %d is not a whole number of blocks", who,
+                    prefix_len);
+    if (prefix_len > 0 && !prefix_blocks)
+        return fail(PKV_EINVAL, "%s: prefix_blocks is NULL", who);
+    if (num_seqs < 0)
+        return fail(PKV_EINVAL, "%s: num_seqs %d", who, num_seqs);
+    if (num_seqs == 0)
+        return PKV_OK;
+    if ((int64_t)num_seqs * num_q_heads > INT32_MAX / 2)
+        return fail(PKV_EINVAL, "%s: too many rows", who);
+    const int32_t nb = prefix_len / c->block_size;
+    const int32_t ks = cascade_splits(num_seqs, num_q_heads, nb, c);
+    const int32_t W = auto_splits(num_seqs, max_context_len, c);
+    const CascadeWs lay = cascade_layout(num_seqs, num_q_heads, c->head_dim, ks, W);
+    if ((rc = check_ptr(workspace, "workspace", who)))
+        return rc;
+    if (workspace_bytes < lay.total)
+        return fail(PKV_EINVAL, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                    lay.total);
+    if ((rc = check_ptr(out, "out", who)))
+        return rc;
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
+        return fail(PKV_EINVAL, "%s: out_dtype %d", who, out_dtype);
+    char *ws = static_cast<char *>(workspace);
+    const int64_t rows = (int64_t)num_seqs * num_q_heads;
+    float *o_all = reinterpret_cast<float *>(ws + lay.o);
+    float *lse_all = reinterpret_cast<float *>(ws + lay.lse);
+    // The suffixes: a plain split decode writing a normalised fp32 state.
+    rc = decode_call(who, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                     num_seqs, num_q_heads, max_context_len, scale,
+                     o_all + (size_t)ks * rows * c->head_dim, PKV_F32, W, ws + lay.dws,
+                     workspace_bytes - lay.dws, c, stream, nullptr, nullptr, nullptr,
+                     lse_all + (size_t)ks * rows);
+    if (rc != PKV_OK)
+        return rc;
+    if (ks > 0) {
+        // The shared prefix once for all sequences: ks pseudo-sequences, one
+        // per range of prefix blocks, each holding every sequence's queries
+        // (read from the same rows) and attending its whole range.
+        const int32_t nbk = (nb + ks - 1) / ks;
+        int32_t *qs = reinterpret_cast<int32_t *>(ws + lay.qs);
+        int32_t *lens = reinterpret_cast<int32_t *>(ws + lay.lens);
+        if ((rc = pkv::launch_cascade_setup(qs, lens, ks, num_seqs, nbk, nb, c->block_size,
+                                            stream)))
+            return rc;
+        pkv::PrefillLaunch p{q, qs, ks, num_seqs, k_cache, v_cache, prefix_blocks, nbk, lens,
+                             nbk * c->block_size, num_q_heads, c->num_kv_heads, c->num_blocks,
+                             c->block_size, c->head_dim, scale, o_all, PKV_F32, stream};
+        p.causal = 0;
+        p.q_shared = 1;
+        p.lse = lse_all;
+        if ((rc = pkv::launch_prefill(p)))
+            return rc;
+    }
+    return pkv::launch_merge_states(o_all, lse_all, ks + 1, rows, c->head_dim, out, out_dtype,
+                                    stream);
 }
 
 extern "C" size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

@@ -97,6 +97,7 @@ struct Args {
     int32_t max_len;                  // context lengths are clamped to this
     int32_t out_dtype;
     float scale_log2;                 // scale * log2(e)
+    float *lse;                       // optional [B][Hq]: log2-sum-exp of the scaled scores
 };
 
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -620,6 +621,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
             if (whole) {
                 store_out(a.out, a.out_dtype, ((int64_t)b * a.Hq + hq0 + h) * D + d,
                           Ls > 0.0f ? O / Ls : 0.0f);
+                if (a.lse && d == 0)
+                    a.lse[(int64_t)b * a.Hq + hq0 + h] = Ls > 0.0f ? M + __log2f(Ls) : -INFINITY;
             } else {
                 const int64_t pr = ((int64_t)g * (a.W + a.B) + wg + b) * G + h;
                 a.ws_o[pr * D + d] = O;
@@ -654,6 +657,8 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
     const int64_t oidx = ((int64_t)b * a.Hq + hq) * D + d;
     if (se == sb) {
         store_out(a.out, a.out_dtype, oidx, 0.0f);
+        if (a.lse && d == 0)
+            a.lse[(int64_t)b * a.Hq + hq] = -INFINITY;
         // Fused append of a sequence with no blocks: no split workgroup
         // visits it, so its new row is written here.
         if (a.k_new && h == 0 && d < 2 * a.row_chunks) {
@@ -705,6 +710,33 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
         M = Mn;
     }
     store_out(a.out, a.out_dtype, oidx, Ls > 0.0f ? O / Ls : 0.0f);
+    if (a.lse && d == 0)
+        a.lse[(int64_t)b * a.Hq + hq] = Ls > 0.0f ? M + __log2f(Ls) : -INFINITY;
+}
+
+// Log-sum-exp merge of K attention states of the same rows (each state a
+// normalised output and its log2-sum-exp), in state order.  One workgroup
+// per row, one thread per output element.
+template <int D>
+__global__ __launch_bounds__(D) void k_merge_states(const float *__restrict__ o,
+                                                    const float *__restrict__ lse, int32_t K,
+                                                    int64_t rows, void *out, int32_t out_dtype)
+{
+    const int64_t r = blockIdx.x;
+    const int d = threadIdx.x;
+    float M = -INFINITY;
+    for (int k = 0; k < K; ++k)
+        M = fmaxf(M, lse[k * rows + r]);
+    float W = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+        for (int k = 0; k < K; ++k) {
+            const float lk = lse[k * rows + r];
+            const float f = (lk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lk - M);
+            W += f;
+            O = __builtin_fmaf(o[(k * rows + r) * D + d], f, O);
+        }
+    }
+    store_out(out, out_dtype, r * D + d, W > 0.0f ? O / W : 0.0f);
 }
 
 using KernelFn = void (*)(Args);
@@ -805,6 +837,7 @@ int launch_decode(const DecodeLaunch &d)
         a.max_len = d.max_context_len;
         a.out_dtype = d.out_dtype;
         a.scale_log2 = d.scale * 1.4426950408889634f;
+        a.lse = d.lse ? d.lse + (int64_t)b0 * d.num_q_heads : nullptr;
         hipLaunchKernelGGL(fn, dim3(d.num_kv_heads, d.num_splits), dim3(kThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -814,6 +847,53 @@ int launch_decode(const DecodeLaunch &d)
         if (e != hipSuccess)
             return fail(PKV_EHIP, "pkv_decode: merge launch failed: %s", hipGetErrorString(e));
     }
+    return PKV_OK;
+}
+
+namespace {
+
+// Query offsets and key counts of the shared-prefix pseudo-sequences of a
+// cascade decode: split k holds prefix blocks [k nbk, min((k+1) nbk, nb)).
+__global__ void k_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int32_t nbk,
+                                int32_t nb, int32_t bs)
+{
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k <= ks)
+        qs[k] = k * B;
+    if (k < ks)
+        lens[k] = min(nbk, nb - k * nbk) * bs;
+}
+
+}  // namespace
+
+int launch_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int32_t nbk,
+                         int32_t nb, int32_t bs, void *stream)
+{
+    hipLaunchKernelGGL(k_cascade_setup, dim3((ks + 64) / 64), dim3(64), 0,
+                       reinterpret_cast<hipStream_t>(stream), qs, lens, ks, B, nbk, nb, bs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(PKV_EHIP, "cascade setup launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
+int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t rows,
+                        int32_t head_dim, void *out, int32_t out_dtype, void *stream)
+{
+    if (rows == 0)
+        return PKV_OK;
+    if (rows > INT32_MAX)
+        return fail(PKV_EINVAL, "merge of %lld rows", (long long)rows);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (head_dim == 64)
+        hipLaunchKernelGGL(k_merge_states<64>, dim3((unsigned)rows), dim3(64), 0, st, o, lse, k,
+                           rows, out, out_dtype);
+    else
+        hipLaunchKernelGGL(k_merge_states<128>, dim3((unsigned)rows), dim3(128), 0, st, o, lse, k,
+                           rows, out, out_dtype);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(PKV_EHIP, "state merge launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
 

@@ -47,8 +47,16 @@ struct DecodeLaunch {
     void *k_cache_w;           // writable views of the caches for the fused append
     void *v_cache_w;
     void *stream;
+    float *lse = nullptr;      // optional [B][Hq] log2-sum-exp of the scaled scores
 };
 int launch_decode(const DecodeLaunch &a);
+// out[r][d] = sum_k o[k][r][d] 2^(lse[k][r] - M) / sum_k 2^(lse[k][r] - M),
+// M = max_k lse[k][r] (zeros where every state is empty), r < rows.
+int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t rows,
+                        int32_t head_dim, void *out, int32_t out_dtype, void *stream);
+// qs[k] = k B (k <= ks), lens[k] = min(nbk, nb - k nbk) bs (k < ks).
+int launch_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int32_t nbk,
+                         int32_t nb, int32_t bs, void *stream);
 // Compute units of the current device (256 if it cannot be queried).
 int32_t device_cu_count();
 
@@ -103,6 +111,9 @@ struct PrefillLaunch {
     void *out;
     int32_t out_dtype;
     void *stream;
+    int32_t causal = 1;        // 0: every row attends all keys of its sequence
+    int32_t q_shared = 0;      // 1: every sequence reads queries from rows 0..C-1
+    float *lse = nullptr;      // optional [rows][Hq] log2-sum-exp of the scaled scores
 };
 int launch_prefill(const PrefillLaunch &a);
 

@@ -81,6 +81,9 @@ struct PArgs {
     void *out;
     int32_t stride, Hq, Hkv, num_blocks, n_qtiles, out_dtype;
     int32_t S;                        // sequences in the launch
+    int32_t causal;                   // 0: every row attends all L keys of its sequence
+    int32_t q_shared;                 // 1: every sequence reads its queries from rows 0..C-1
+    float *lse;                       // optional [rows][Hq]: log2-sum-exp of the scaled scores
     float scale_log2;
 };
 
@@ -175,25 +178,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     if (tok0 >= C)
         return;
     const int tok_end = min(C, tok0 + TQ);
-    const int kend = min(L, p0 + tok_end);           // keys any row of this tile attends
+    const int kend = a.causal ? min(L, p0 + tok_end) : L;   // keys any row of this tile attends
     const int NT = kend > 0 ? (kend + KT - 1) / KT : 0;
 
     // This lane's two query columns (one per 16-row MFMA tile).
     int lim[2];
     bool valid[2];
-    int64_t qrow[2];
+    int64_t qrow[2], qin[2];
+    const int qbase = a.q_shared ? 0 : q0;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
         const int r = w * 32 + ct * 16 + n;
         const int tok = tok0 + r / G;
         valid[ct] = tok < tok_end;
-        lim[ct] = valid[ct] ? p0 + tok : -1;
+        lim[ct] = valid[ct] ? (a.causal ? p0 + tok : L - 1) : -1;
         qrow[ct] = ((int64_t)(q0 + tok) * a.Hq + g * G + r % G) * D;
+        qin[ct] = ((int64_t)(qbase + tok) * a.Hq + g * G + r % G) * D;
     }
-    // Smallest causal limit over the wave's valid rows (wave-uniform): a
-    // tile entirely at or below it needs no mask.
+    // Smallest key limit over the wave's valid rows (wave-uniform): a tile
+    // entirely at or below it needs no mask.
     const int wtok = tok0 + (w * 32) / G;
-    const int lim_w = wtok < tok_end ? p0 + wtok : 0x7FFFFFFF;
+    const int lim_w = wtok < tok_end ? (a.causal ? p0 + wtok : L - 1) : 0x7FFFFFFF;
 
     // Scores enter the exponent as fma(s, c, -m) with c = |scale| log2(e):
     // for a negative scale the q operand's sign bits are flipped (exact), so
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
         for (int ds = 0; ds < NDS; ++ds) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (valid[ct]) {
-                v = *reinterpret_cast<const uint4 *>(a.q + qrow[ct] + ds * 32 + quad * 8);
+                v = *reinterpret_cast<const uint4 *>(a.q + qin[ct] + ds * 32 + quad * 8);
                 v.x ^= qsign;
                 v.y ^= qsign;
                 v.z ^= qsign;
@@ -456,6 +461,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
         if (!valid[ct])
             continue;
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        if (a.lse && quad == 0)
+            a.lse[qrow[ct] / D] = l > 0.0f ? m[ct] + __log2f(l) : -INFINITY;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const int64_t idx = qrow[ct] + dt * 16 + quad * 4;
@@ -525,6 +532,9 @@ int launch_prefill(const PrefillLaunch &p)
     a.S = p.num_seqs;
     a.out_dtype = p.out_dtype;
     a.scale_log2 = p.scale * 1.4426950408889634f;
+    a.causal = p.causal;
+    a.q_shared = p.q_shared;
+    a.lse = p.lse;
     hipStream_t st = reinterpret_cast<hipStream_t>(p.stream);
     hipLaunchKernelGGL(fn, dim3(p.num_kv_heads, (unsigned)nqt, p.num_seqs), dim3(kThreads), 0, st,
                        a);

@@ -177,3 +177,20 @@ def test_copy_blocks_rejects():
     assert call(n=0, sk=None, si=None) == pkv.OK                 # empty list: no-op
     # Only the block shape must agree: the caches may differ in size.
     assert call(n=0, dd=_desc(num_blocks=3)) == pkv.OK
+
+
+def test_decode_cascade_rejects():
+    f = L.pkv_decode_cascade
+
+    def call(desc=None, P=32, pb=FAKE, ws=FAKE, wsb=1 << 30, B=2):
+        d = desc or _desc()
+        return f(FAKE, FAKE, FAKE, pb, P, FAKE, 8, FAKE, B, 64, 100, 0.1, FAKE, pkv.F32, ws, wsb,
+                 ctypes.byref(d), None)
+    assert call(desc=_desc(dtype=pkv.F32)) == pkv.EUNSUPPORTED
+    assert call(P=20) == pkv.EINVAL                    # not a whole number of blocks
+    assert call(P=-16) == pkv.EINVAL
+    assert call(pb=None) == pkv.EINVAL
+    assert call(wsb=64) == pkv.EINVAL                  # short workspace
+    assert call(ws=None) == pkv.EINVAL
+    assert call(B=0) == pkv.OK
+    assert L.pkv_decode_cascade_workspace_bytes(2, 64, 32, 100, ctypes.byref(_desc())) > 0
