@@ -198,7 +198,9 @@ int decode_call(const char *who, const void *q, const void *k_cache, const void 
         return fail(PKV_EINVAL,
                     "%s: max_context_len %d must lie in [0, block_table_stride %d * block_size]",
                     who, max_context_len, block_table_stride);
-    if (blocks_bound(num_seqs, max_context_len, c) > INT32_MAX)
+    if (blocks_bound(num_seqs, max_context_len, c) +
+            (int64_t)pkv::decode_piece_cost(c->block_size, c->head_dim, elem_size(c->dtype)) *
+                pkv::kDecodeMaxSeqs > INT32_MAX)
         return fail(PKV_EINVAL, "%s: %d sequences of up to %d tokens exceed 2^31 blocks per launch",
                     who, num_seqs, max_context_len);
     if (num_splits < 0 || num_splits > 65535)

@@ -98,6 +98,7 @@ struct Args {
     int32_t out_dtype;
     float scale_log2;                 // scale * log2(e)
     float *lse;                       // optional [B][Hq]: log2-sum-exp of the scaled scores
+    int32_t piece_cost;               // cost of a sequence boundary, in blocks (see cost_at)
 };
 
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -202,18 +203,45 @@ __device__ __forceinline__ int clamp_len(const Args &a, int b)
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// Workgroup whose range holds flattened block x: ranges are
-// [floor(T w / W), floor(T (w+1) / W)).
-__device__ __forceinline__ int owner(int64_t x, int64_t T, int W)
+// Balanced ranges.  Flattened block x of sequence b costs x + pc * b:
+// besides its blocks, a workgroup pays a fixed time at every sequence
+// boundary in its range (the load pipeline drains and refills, q and block
+// ids are staged, the waves merge), measured at 4-6 us on MI355X, the time
+// to stream ~144 KiB at one workgroup's share of the bandwidth; pc is that
+// in blocks (a sweep of 8 to 256 KiB put the optimum there).  The cost line [0, Ct), Ct = T + pc * B, is cut into W equal
+// ranges [floor(Ct w / W), floor(Ct (w+1) / W)), so workgroups whose ranges
+// cross more boundaries get fewer blocks.
+__device__ __forceinline__ int64_t cost_at(int64_t x, int b, int pc)
 {
-    return (int)(((x + 1) * W + T - 1) / T - 1);
+    return x + (int64_t)pc * b;
 }
 
-// Whether workgroup w got no blocks (possible when W exceeds the batch's
-// block count); it then wrote no piece.
-__device__ __forceinline__ bool empty_range(int w, int64_t T, int W)
+// Workgroup whose range holds cost c.
+__device__ __forceinline__ int owner(int64_t c, int64_t Ct, int W)
 {
-    return T * w / W == T * (w + 1) / W;
+    return (int)(((c + 1) * W + Ct - 1) / Ct - 1);
+}
+
+// Whether the cost range of workgroup w is empty (possible when W exceeds
+// Ct); a range between two costs of one sequence is never empty otherwise.
+__device__ __forceinline__ bool empty_range(int w, int64_t Ct, int W)
+{
+    return Ct * w / W == Ct * (w + 1) / W;
+}
+
+// First flattened block whose cost is >= c (T if none).
+__device__ __forceinline__ int block_at_cost(const int32_t *pref, int B, int pc, int64_t c)
+{
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cost_at(pref[mid], mid, pc) <= c)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int64_t x = pref[lo] + (c - cost_at(pref[lo], lo, pc));
+    return (int)(x < pref[lo + 1] ? x : pref[lo + 1]);
 }
 
 template <int DT, int D, int BS, int G>
@@ -274,7 +302,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
         for (int i = tid; i <= a.B; i += kThreads)
             a.ws_pref[i] = lds_pref[i];
 
-    const int64_t start = (int64_t)T * wg / a.W, end = (int64_t)T * (wg + 1) / a.W;
+    const int64_t Ct = (int64_t)T + (int64_t)a.piece_cost * a.B;
+    const int64_t start = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * wg / a.W);
+    const int64_t end = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * (wg + 1) / a.W);
     if (start >= end)
         return;
 
@@ -601,7 +631,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
         __syncthreads();
 
         // Merge the 4 waves; a sequence held whole by this range is final.
-        const bool whole = owner(sb, T, a.W) == owner(se - 1, T, a.W);
+        const bool whole = owner(cost_at(sb, b, a.piece_cost), Ct, a.W) ==
+                           owner(cost_at(se - 1, b, a.piece_cost), Ct, a.W);
         for (int idx = tid; idx < G * D; idx += kThreads) {
             const int h = idx / D, d = idx % D;
             float M = -INFINITY;
@@ -652,7 +683,7 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
     const int b = blockIdx.x, hq = blockIdx.y, d = threadIdx.x;
     const int G = a.Hq / a.Hkv;
     const int g = hq / G, h = hq - g * G;
-    const int T = a.ws_pref[a.B];
+    const int64_t Ct = (int64_t)a.ws_pref[a.B] + (int64_t)a.piece_cost * a.B;
     const int sb = a.ws_pref[b], se = a.ws_pref[b + 1];
     const int64_t oidx = ((int64_t)b * a.Hq + hq) * D + d;
     if (se == sb) {
@@ -672,10 +703,11 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
         }
         return;
     }
-    const int wf = owner(sb, T, a.W), wl = owner(se - 1, T, a.W);
+    const int wf = owner(cost_at(sb, b, a.piece_cost), Ct, a.W);
+    const int wl = owner(cost_at(se - 1, b, a.piece_cost), Ct, a.W);
     if (wf == wl)
         return;
-    const bool sparse = T < a.W;   // only then can a range be empty
+    const bool sparse = Ct < a.W;   // only then can a range be empty
     // Piece (w + b) of KV head g, query head h within the group.  Pieces
     // are read 8 at a time, all loads of a batch in flight together, and
     // folded into a running (M, L, O) in workgroup order.
@@ -686,7 +718,7 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int w = w0 + k;
-            const bool use = w <= wl && !(sparse && empty_range(w, T, a.W));
+            const bool use = w <= wl && !(sparse && empty_range(w, Ct, a.W));
             const int64_t pr = p0 + (int64_t)w * G;
             mp[k] = use ? a.ws_ml[pr * 2] : -INFINITY;
             lp[k] = use ? a.ws_ml[pr * 2 + 1] : 0.0f;
@@ -788,6 +820,12 @@ int32_t device_cu_count()
     return cached[dev];
 }
 
+int32_t decode_piece_cost(int32_t block_size, int32_t head_dim, int32_t elem_size)
+{
+    const int32_t pc = 147456 / (2 * block_size * head_dim * elem_size);
+    return pc < 1 ? 1 : pc;
+}
+
 int launch_decode(const DecodeLaunch &d)
 {
     if (d.num_seqs == 0)
@@ -838,6 +876,7 @@ int launch_decode(const DecodeLaunch &d)
         a.out_dtype = d.out_dtype;
         a.scale_log2 = d.scale * 1.4426950408889634f;
         a.lse = d.lse ? d.lse + (int64_t)b0 * d.num_q_heads : nullptr;
+        a.piece_cost = decode_piece_cost(d.block_size, d.head_dim, esz);
         hipLaunchKernelGGL(fn, dim3(d.num_kv_heads, d.num_splits), dim3(kThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)

@@ -50,6 +50,8 @@ struct DecodeLaunch {
     float *lse = nullptr;      // optional [B][Hq] log2-sum-exp of the scaled scores
 };
 int launch_decode(const DecodeLaunch &a);
+// Cost of a sequence boundary in a decode workgroup's range, in blocks.
+int32_t decode_piece_cost(int32_t block_size, int32_t head_dim, int32_t elem_size);
 // out[r][d] = sum_k o[k][r][d] 2^(lse[k][r] - M) / sum_k 2^(lse[k][r] - M),
 // M = max_k lse[k][r] (zeros where every state is empty), r < rows.
 int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t rows,
