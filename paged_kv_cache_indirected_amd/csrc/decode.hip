@@ -244,6 +244,134 @@ __device__ __forceinline__ int block_at_cost(const int32_t *pref, int B, int pc,
     return (int)(x < pref[lo + 1] ? x : pref[lo + 1]);
 }
 
+// One 16-token unit of the split pass: S = K Q^T on MFMA, the online
+// softmax update of (o, m, l) in log2 units, O^T += V^T P^T on MFMA.  kr / vr
+// hold the unit's K and V chunks as loaded, qr the B operand of the group's
+// q rows; pos0 is the position of this lane's first token (4 g4 of the
+// unit), `full` says every token of the unit lies inside the context.
+template <int DT, int D, int G>
+__device__ __forceinline__ void unit_math(const uint4 (&kr)[D / (16 / (DT == PKV_F32 ? 4 : 2)) / 4],
+                                          uint4 (&vr)[DT == PKV_F32 ? D / 16 : D / 32],
+                                          const uint4 (&qr)[D / (16 / (DT == PKV_F32 ? 4 : 2)) / 4],
+                                          f32x4 (&o)[D / 16], float &m, float &l, int pos0,
+                                          int L, bool ok, bool full, float scale_log2)
+{
+    constexpr int NKL = D / (16 / (DT == PKV_F32 ? 4 : 2)) / 4;
+    constexpr int NVL = DT == PKV_F32 ? D / 16 : D / 32;
+    constexpr int NACC = D / 16;
+    // S for tokens 4 g4 .. 4 g4 + 3 of head n.
+    f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < NKL; ++kk) {
+        if constexpr (DT == PKV_F32) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].x), as_f32(qr[kk].x),
+                                                        sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].y), as_f32(qr[kk].y),
+                                                        sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].z), as_f32(qr[kk].z),
+                                                        sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].w), as_f32(qr[kk].w),
+                                                        sacc, 0, 0, 0);
+        } else {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, kr[kk]), __builtin_bit_cast(bf16x8, qr[kk]),
+                sacc, 0, 0, 0);
+        }
+    }
+
+    // Scores in log2 units; positions past the context are masked.
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s[i] = sacc[i] * scale_log2;
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[i] = (ok && pos0 + i < L) ? s[i] : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mt = xrow<16, true>(mt);
+    mt = xrow<32, true>(mt);
+    const bool up = mt > m + kLazyMax;
+    const float mn = up ? mt : m;
+    const float alpha = up ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+    const bool dead = (mn == -INFINITY);
+    float p[4], sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i] = dead ? 0.0f : __builtin_amdgcn_exp2f(s[i] - mn);
+        sum += p[i];
+    }
+    l = __builtin_fmaf(l, alpha, sum);
+    m = mn;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+        for (int i = 0; i < NACC; ++i)
+            o[i] *= alpha;
+    }
+
+    // Unused slots past the context end hold arbitrary bits (NaN
+    // poison): zero their V so that 0 * NaN never reaches the sum.
+    if (!full && ok) {
+        const int nv = L - pos0;                     // valid tokens of this quarter
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            if constexpr (DT == PKV_F32) {
+                vr[u].x = nv > 0 ? vr[u].x : 0u;
+                vr[u].y = nv > 1 ? vr[u].y : 0u;
+                vr[u].z = nv > 2 ? vr[u].z : 0u;
+                vr[u].w = nv > 3 ? vr[u].w : 0u;
+            } else {
+                const uint32_t m01 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+                const uint32_t m23 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+                vr[u].x &= m01;
+                vr[u].y &= m23;
+                vr[u].z &= m01;
+                vr[u].w &= m23;
+            }
+        }
+    }
+
+    // O^T += V^T P^T.
+    if constexpr (DT == PKV_F32) {
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].x), p[0], o[u], 0, 0, 0);
+            o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].y), p[1], o[u], 0, 0, 0);
+            o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].z), p[2], o[u], 0, 0, 0);
+            o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].w), p[3], o[u], 0, 0, 0);
+        }
+    } else {
+        // hi = p truncated to bf16 (its top 16 bits, exact in fp32),
+        // lo = bf16(p - hi).
+        uint32_t pu[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pu[i] = __builtin_bit_cast(uint32_t, p[i]);
+        const uint32_t h01 = __builtin_amdgcn_perm(pu[1], pu[0], 0x07060302u);
+        const uint32_t h23 = __builtin_amdgcn_perm(pu[3], pu[2], 0x07060302u);
+        const uint32_t l01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+            f32x2{p[0] - as_f32(pu[0] & 0xFFFF0000u), p[1] - as_f32(pu[1] & 0xFFFF0000u)},
+            bf16x2_t));
+        const uint32_t l23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+            f32x2{p[2] - as_f32(pu[2] & 0xFFFF0000u), p[3] - as_f32(pu[3] & 0xFFFF0000u)},
+            bf16x2_t));
+        const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
+        const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[u].x, vr[u].y));
+            const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[u].z, vr[u].w));
+            o[2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, phi, o[2 * u], 0, 0, 0);
+            o[2 * u + 1] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v1, phi, o[2 * u + 1], 0, 0, 0);
+            o[2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, plo, o[2 * u], 0, 0, 0);
+            o[2 * u + 1] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v1, plo, o[2 * u + 1], 0, 0, 0);
+        }
+    }
+}
+
 template <int DT, int D, int BS, int G>
 __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
 {
@@ -447,119 +575,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
                 }
             }
 
-            // S for tokens 4 g4 .. 4 g4 + 3 of head n.
-            f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < NKL; ++kk) {
-                if constexpr (DT == PKV_F32) {
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].x), as_f32(qr[kk].x),
-                                                                sacc, 0, 0, 0);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].y), as_f32(qr[kk].y),
-                                                                sacc, 0, 0, 0);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].z), as_f32(qr[kk].z),
-                                                                sacc, 0, 0, 0);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kr[kk].w), as_f32(qr[kk].w),
-                                                                sacc, 0, 0, 0);
-                } else {
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, kr[kk]), __builtin_bit_cast(bf16x8, qr[kk]),
-                        sacc, 0, 0, 0);
-                }
-            }
-
-            // Scores in log2 units; positions past the context are masked.
-            const int pos0 = ubase + 4 * g4;
-            const bool full = ok && (j + 1) * BS <= L;      // wave-uniform
-            float s[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s[i] = sacc[i] * a.scale_log2;
-            if (!full) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s[i] = (ok && pos0 + i < L) ? s[i] : -INFINITY;
-            }
-            float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-            mt = xrow<16, true>(mt);
-            mt = xrow<32, true>(mt);
-            const bool up = mt > m + kLazyMax;
-            const float mn = up ? mt : m;
-            const float alpha = up ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-            const bool dead = (mn == -INFINITY);
-            float p[4], sum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = dead ? 0.0f : __builtin_amdgcn_exp2f(s[i] - mn);
-                sum += p[i];
-            }
-            l = __builtin_fmaf(l, alpha, sum);
-            m = mn;
-            if (__builtin_amdgcn_ballot_w64(up) != 0) {
-#pragma unroll
-                for (int i = 0; i < NACC; ++i)
-                    o[i] *= alpha;
-            }
-
-            // Unused slots past the context end hold arbitrary bits (NaN
-            // poison): zero their V so that 0 * NaN never reaches the sum.
-            if (!full && ok) {
-                const int nv = L - pos0;                     // valid tokens of this quarter
-#pragma unroll
-                for (int u = 0; u < NVL; ++u) {
-                    if constexpr (DT == PKV_F32) {
-                        vr[u].x = nv > 0 ? vr[u].x : 0u;
-                        vr[u].y = nv > 1 ? vr[u].y : 0u;
-                        vr[u].z = nv > 2 ? vr[u].z : 0u;
-                        vr[u].w = nv > 3 ? vr[u].w : 0u;
-                    } else {
-                        const uint32_t m01 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
-                        const uint32_t m23 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
-                        vr[u].x &= m01;
-                        vr[u].y &= m23;
-                        vr[u].z &= m01;
-                        vr[u].w &= m23;
-                    }
-                }
-            }
-
-            // O^T += V^T P^T.
-            if constexpr (DT == PKV_F32) {
-#pragma unroll
-                for (int u = 0; u < NVL; ++u) {
-                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].x), p[0], o[u], 0, 0, 0);
-                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].y), p[1], o[u], 0, 0, 0);
-                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].z), p[2], o[u], 0, 0, 0);
-                    o[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vr[u].w), p[3], o[u], 0, 0, 0);
-                }
-            } else {
-                // hi = p truncated to bf16 (its top 16 bits, exact in fp32),
-                // lo = bf16(p - hi).
-                uint32_t pu[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pu[i] = __builtin_bit_cast(uint32_t, p[i]);
-                const uint32_t h01 = __builtin_amdgcn_perm(pu[1], pu[0], 0x07060302u);
-                const uint32_t h23 = __builtin_amdgcn_perm(pu[3], pu[2], 0x07060302u);
-                const uint32_t l01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                    f32x2{p[0] - as_f32(pu[0] & 0xFFFF0000u), p[1] - as_f32(pu[1] & 0xFFFF0000u)},
-                    bf16x2_t));
-                const uint32_t l23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                    f32x2{p[2] - as_f32(pu[2] & 0xFFFF0000u), p[3] - as_f32(pu[3] & 0xFFFF0000u)},
-                    bf16x2_t));
-                const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
-                const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
-#pragma unroll
-                for (int u = 0; u < NVL; ++u) {
-                    const s16x4 v0 = __builtin_bit_cast(s16x4, make_uint2(vr[u].x, vr[u].y));
-                    const s16x4 v1 = __builtin_bit_cast(s16x4, make_uint2(vr[u].z, vr[u].w));
-                    o[2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, phi, o[2 * u], 0, 0, 0);
-                    o[2 * u + 1] =
-                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v1, phi, o[2 * u + 1], 0, 0, 0);
-                    o[2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, plo, o[2 * u], 0, 0, 0);
-                    o[2 * u + 1] =
-                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v1, plo, o[2 * u + 1], 0, 0, 0);
-                }
-            }
+            unit_math<DT, D, G>(kr, vr, qr, o, m, l, ubase + 4 * g4, L, ok,
+                                ok && (j + 1) * BS <= L, a.scale_log2);
         };
 
         // Wave w takes blocks j0 + w, j0 + w + NW, ... of the piece, each as
