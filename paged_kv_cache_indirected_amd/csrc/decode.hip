@@ -372,8 +372,11 @@ __device__ __forceinline__ void unit_math(const uint4 (&kr)[D / (16 / (DT == PKV
     }
 }
 
+// fp32 caches at head_dim 128 need more than half the register file for the
+// load ring and accumulators: one workgroup per CU (the grid is sized so
+// anyway) lets them have it instead of spilling.
 template <int DT, int D, int BS, int G>
-__global__ __launch_bounds__(kThreads, 2) void k_decode(Args a)
+__global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void k_decode(Args a)
 {
     using Sh = Shape<DT, D, BS, G>;
     constexpr int LPT = Sh::LPT, NKL = Sh::NKL, NVL = Sh::NVL, NACC = Sh::NACC;
