@@ -338,9 +338,29 @@ def bench_cfg5(timer, splits):
         pkv.append(ds["k_new"], ds["v_new"], ds["slots"], dc.k_cache, dc.v_cache, dc.desc)
         prefill()
         decode()
+    # The same step with the decode on a second stream (default priority):
+    # the MFMA-bound prefill and the HBM-bound decode run side by side.
+    side = torch.cuda.Stream()
+
+    def step_two_streams():
+        main = torch.cuda.current_stream()
+        ev0 = torch.cuda.Event()
+        ev0.record(main)
+        side.wait_event(ev0)
+        pkv.append(ck, cv, cslots, pc.k_cache, pc.v_cache, pc.desc)
+        prefill()
+        with torch.cuda.stream(side):
+            pkv.append(ds["k_new"], ds["v_new"], ds["slots"], dc.k_cache, dc.v_cache, dc.desc,
+                       stream=side)
+            pkv.decode(ds["q"], dc.k_cache, dc.v_cache, ds["tables"], ds["lens"], sh.scale, dout,
+                       dc.desc, ds["max_len"], workspace=ws, num_splits=splits, stream=side)
+        ev1 = torch.cuda.Event()
+        ev1.record(side)
+        main.wait_event(ev1)
     t_pre = float(np.median(timer.per_call(prefill, 10)))
     t_dec = float(np.median(timer.per_call(decode, 20)))
     t_step = float(np.median(timer.per_call(step, 10)))
+    t_step2 = float(np.median(timer.per_call(step_two_streams, 10)))
     flops = sum(4.0 * sh.Hq * sh.D * (int(c) * int(p) + int(c) * (int(c) + 1) / 2)
                 for p, c in zip(pre.prior, pre.chunk))
     dbytes = float(dec.lens.sum()) * kv_row_bytes(sh)
@@ -356,7 +376,10 @@ def bench_cfg5(timer, splits):
             "decode_kv_GBps": round(dbytes / t_dec / 1e9, 1),
             "step_ms": round(1e3 * t_step, 4),
             "step_note": "append of 2048 chunk rows + 64 decode rows, prefill, decode; "
-                         "one stream"}
+                         "one stream",
+            "step_two_streams_ms": round(1e3 * t_step2, 4),
+            "step_two_streams_note": "prefill (with its append) on the launch stream, decode "
+                                     "(with its append) on a second stream, joined by events"}
 
 
 def bench_block_copy(timer):
