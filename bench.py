@@ -382,6 +382,41 @@ def bench_cfg5(timer, splits):
                                      "(with its append) on a second stream, joined by events"}
 
 
+def bench_append(timer):
+    """pkv_append in bulk: rows written to random distinct slots of a large
+    cache (a prefill chunk's worth of rows per sequence, many sequences), and
+    the decode step's shape (one row per sequence, 256 sequences)."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    Hkv, bs, D = 8, 16, 128
+    nb = 16384
+    desc = pkv.CacheDesc(nb, Hkv, bs, D, pkv.BF16)
+    kc = torch.zeros(desc.cache_shape(), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    g = np.random.default_rng(23)
+    res = {}
+    for label, T, contiguous in (("random_slots", 65536, False), ("chunk_runs", 65536, True),
+                                 ("decode_step", 256, False)):
+        if contiguous:   # whole blocks in order: 512-token chunks of 128 sequences
+            blocks = g.permutation(nb)[:T // bs]
+            slots = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+        else:
+            slots = g.permutation(nb * bs)[:T]
+        sl = torch.tensor(slots.astype(np.int32), device="cuda")
+        k = torch.randn((T, Hkv, D), device="cuda").to(torch.bfloat16)
+        v = torch.randn((T, Hkv, D), device="cuda").to(torch.bfloat16)
+        t = float(np.median(timer.per_call(
+            lambda: pkv.append(k, v, sl, kc, vc, desc), 30)))
+        nbytes = 2 * T * Hkv * D * 2 * 2          # K and V rows read, and written
+        res[label] = {"rows": T, "ms_per_call": round(1e3 * t, 4),
+                      "GBps_read_plus_write": round(nbytes / t / 1e9, 1),
+                      "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    res["workload"] = ("pkv_append: rows [T][8][128] bf16 into a 16384-block cache, slots random "
+                       "and distinct, or whole blocks in order (prefill chunks), or one row per "
+                       "sequence for 256 sequences (a decode step)")
+    return res
+
+
 def bench_block_copy(timer):
     """pkv_copy_blocks: copy-on-write style copies inside one cache, and a
     sequence's blocks swapped out to pinned host memory and back."""
@@ -646,7 +681,7 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads and the probes")
     ap.add_argument("--only", choices=["continuous_batching", "prefix_sharing",
-                                       "chunked_prefill_mixed", "block_copy",
+                                       "chunked_prefill_mixed", "append", "block_copy",
                                        "prefix_cache_ttft", "step_scheduler"],
                     help="run one secondary workload alone (for profiling) and print its JSON")
     ap.add_argument("--probe-copy", action="store_true",
@@ -679,6 +714,7 @@ def main():
         fns = {"continuous_batching": lambda: bench_cfg3(timer, 10, args.splits),
                "prefix_sharing": lambda: bench_cfg4(timer, args.splits),
                "chunked_prefill_mixed": lambda: bench_cfg5(timer, args.splits),
+               "append": lambda: bench_append(timer),
                "block_copy": lambda: bench_block_copy(timer),
                "prefix_cache_ttft": lambda: bench_prefix_ttft(timer),
                "step_scheduler": lambda: bench_sched()}
@@ -807,6 +843,9 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] chunked prefill + decode")
         wl["chunked_prefill_mixed"] = bench_cfg5(timer, args.splits)
+        torch.cuda.empty_cache()
+        log("[bench] append")
+        wl["append"] = bench_append(timer)
         torch.cuda.empty_cache()
         log("[bench] block copy and swap")
         wl["block_copy"] = bench_block_copy(timer)

@@ -6,11 +6,11 @@
 // the tile of KV head g (tiles are [num_blocks][Hkv], BS x D elements each).
 // Tile layout: K keeps each token's dims in 16-byte chunks, chunk c of
 // token o at (c * BS + o) * 16 bytes; V keeps groups of 4 tokens together
-// per dim, element (o, d) at ((o / 4) * D + d) * 4 + o % 4.  One thread
-// moves one 16-byte chunk of the K row (a single 16-byte store) and the
-// matching chunk of the V row (E element stores, E = 16 / element size);
-// consecutive threads cover consecutive chunks of a row, so the row reads
-// are coalesced.  HBM bound: 2 * T * Hkv * D * elem bytes each way.
+// per dim, element (o, d) at ((o / 4) * D + d) * 4 + o % 4.  Thread c of a
+// row moves the row's 16-byte K chunk c (one 16-byte store) and its V
+// elements c, c + R, c + 2R, ... (R = 16-byte chunks per row), so that at
+// every store the lanes of a row write consecutive dims.  HBM bound:
+// 2 * T * Hkv * D * elem bytes each way.
 #include <hip/hip_runtime.h>
 
 #include "pkv_internal.h"
@@ -22,35 +22,18 @@ constexpr int kThreads = 256;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Store V chunk c (E consecutive dims of token offset o) into a V tile.
-template <int D, int ES, int BS>
-__device__ __forceinline__ void store_v_chunk(char *tile, int o, int c, const u32x4 &x)
-{
-    constexpr int E = 16 / ES;
-    const int base = (o / 4) * D * 4 + o % 4;          // element index of (o, d = 0)
-    if constexpr (ES == 4) {
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            reinterpret_cast<uint32_t *>(tile)[base + (c * E + e) * 4] = x[e];
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            reinterpret_cast<uint16_t *>(tile)[base + (c * E + e) * 4] =
-                (uint16_t)(x[e / 2] >> (16 * (e & 1)));
-    }
-}
-
 // All index math is 32-bit; the host guarantees T * Hkv * ROWC and
 // num_blocks * BS fit.
 template <int D, int ES, int BS>
 __global__ __launch_bounds__(kThreads) void k_append(const uint4 *__restrict__ k,
-                                                     const uint4 *__restrict__ v,
+                                                     const char *__restrict__ v,
                                                      const int32_t *__restrict__ slots,
                                                      char *__restrict__ kc, char *__restrict__ vc,
                                                      int32_t total_chunks, int32_t heads,
                                                      int32_t cap_slots)
 {
     constexpr int ROWC = D * ES / 16;                   // 16-byte chunks per row
+    constexpr int E = 16 / ES;                          // elements per chunk
     constexpr int TILE = BS * D * ES;                   // bytes per (block, head) tile
     const int32_t i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= total_chunks)
@@ -59,18 +42,38 @@ __global__ __launch_bounds__(kThreads) void k_append(const uint4 *__restrict__ k
     const int32_t c = i % ROWC;
     const int32_t t = row / heads;
     const int32_t g = row - t * heads;
-    // The row loads do not depend on the slot: issue all three together so
-    // the copy costs one memory latency, not two in a chain.
+    // K: this thread's 16-byte chunk.  V: the row's elements c, c + ROWC,
+    // c + 2 ROWC, ... so that the lanes of a row handle consecutive dims at
+    // every step (their stores land 8 or 16 bytes apart, in a few runs).
+    // The row loads do not depend on the slot: issue them all before it is
+    // known, so the copy costs one memory latency, not two in a chain.
     const u32x4 kk = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(k) + i);
-    const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(v) + i);
+    const char *vrow = v + (int64_t)row * D * ES;
+    uint32_t vv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if constexpr (ES == 4)
+            vv[e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(vrow) + c + e * ROWC);
+        else
+            vv[e] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(vrow) + c + e * ROWC);
+    }
     const int32_t s = slots[t];
-    asm volatile("" ::"v"(kk), "v"(vv));   // keep the row loads ahead of the branch
+    asm volatile("" ::"v"(kk));            // keep the row loads ahead of the branch
     if (s < 0 || s >= cap_slots)           // padding, or outside the cache: not written
         return;
     const int32_t blk = s / BS, o = s % BS;
     const int64_t tile = ((int64_t)blk * heads + g) * TILE;
     *reinterpret_cast<u32x4 *>(kc + tile + (c * BS + o) * 16) = kk;
-    store_v_chunk<D, ES, BS>(vc + tile, o, c, vv);
+    // V element (o, d) of the tile sits at ((o / 4) * D + d) * 4 + o % 4.
+    const int base = (o / 4) * D * 4 + o % 4;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int idx = base + (c + e * ROWC) * 4;
+        if constexpr (ES == 4)
+            reinterpret_cast<uint32_t *>(vc + tile)[idx] = vv[e];
+        else
+            reinterpret_cast<uint16_t *>(vc + tile)[idx] = (uint16_t)vv[e];
+    }
 }
 
 template <int D, int ES>
@@ -79,7 +82,7 @@ int launch_shape(const AppendLaunch &a, int32_t total, hipStream_t st)
     const unsigned grid = (unsigned)((total + kThreads - 1) / kThreads);
     const int32_t cap = a.num_blocks * a.block_size;
     auto kp = static_cast<const uint4 *>(a.k);
-    auto vp = static_cast<const uint4 *>(a.v);
+    auto vp = static_cast<const char *>(a.v);
     auto kc = static_cast<char *>(a.k_cache);
     auto vc = static_cast<char *>(a.v_cache);
     if (a.block_size == 16)
