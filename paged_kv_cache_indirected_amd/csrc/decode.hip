@@ -65,7 +65,7 @@ constexpr int NW = 4;                 // waves per workgroup
 constexpr int kThreads = NW * 64;
 constexpr float kLazyMax = 8.0f;      // running-max slack, log2 units
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data format, no swizzle
-constexpr int kIdChunk = 512;         // block-table entries staged in LDS at a time
+constexpr int kIdChunk = 2 * kThreads; // block-table entries staged in LDS at a time
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -102,6 +102,17 @@ struct Args {
 };
 
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// Workgroup barrier ordering LDS only.  Waves of a workgroup exchange data
+// through LDS alone (global stores here are read by later launches), so the
+// barrier need not wait for outstanding global stores as __syncthreads()
+// does.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <int DT, int D, int BS, int G>
 struct Shape {
@@ -410,7 +421,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         }
         if (lane == 63)
             lds_wsum[w] = v;
-        __syncthreads();
+        lds_barrier();
         int before = 0, tot = 0;
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
@@ -421,11 +432,11 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         if (b < a.B)
             lds_pref[b + 1] = carry + before + v;
         carry += tot;
-        __syncthreads();
+        lds_barrier();
     }
     if (tid == 0)
         lds_pref[0] = 0;
-    __syncthreads();
+    lds_barrier();
     const int T = lds_pref[a.B];
     const int hq0 = g * G;
 
@@ -472,26 +483,45 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         const int nblk = se - sb;
         const int32_t *bt = a.tables + (int64_t)b * a.stride;
 
-        // The group's q rows (G * D elements) go to LDS.
+        // One round trip brings the group's q rows (G * D elements), the
+        // piece's first block ids and, for the fused append, the step's new
+        // K/V rows of this KV head and their slot: all loads are issued
+        // before any is waited for.  The workgroup holding the sequence's
+        // last block writes the new rows to their slot and keeps them in LDS
+        // so that the attention reads position L-1 from there rather than
+        // from the cache written in the same launch.
+        const int n0 = j1 - j0 < kIdChunk ? j1 - j0 : kIdChunk;
+        const bool last_piece = a.k_new && j1 == nblk;
+        int32_t nslot = -1;
         {
-            const uint4 *qp = static_cast<const uint4 *>(a.q) + ((int64_t)b * a.Hq + hq0) * LPT;
-            for (int i = tid; i < G * LPT; i += kThreads)
-                lds_q[i] = qp[i];
+            static_assert(G * LPT <= kThreads && kIdChunk == 2 * kThreads, "staging shape");
+            uint4 qv = make_uint4(0, 0, 0, 0), nv = make_uint4(0, 0, 0, 0);
+            int32_t id0 = -1, id1 = -1;
+            if (tid < G * LPT)
+                qv = static_cast<const uint4 *>(a.q)[((int64_t)b * a.Hq + hq0) * LPT + tid];
+            if (tid < n0)
+                id0 = bt[j0 + tid];
+            if (tid + kThreads < n0)
+                id1 = bt[j0 + tid + kThreads];
+            if (last_piece) {
+                nslot = a.slots[b];
+                if (tid < 2 * LPT)
+                    nv = static_cast<const uint4 *>(tid < LPT ? a.k_new : a.v_new)
+                        [((int64_t)b * a.Hkv + g) * LPT + tid % LPT];
+            }
+            if (tid < G * LPT)
+                lds_q[tid] = qv;
+            if (tid < n0)
+                lds_ids[tid] = id0;
+            if (tid + kThreads < n0)
+                lds_ids[tid + kThreads] = id1;
+            if ((unsigned)nslot < (unsigned)(a.num_blocks * BS) && tid < 2 * LPT) {
+                lds_new[tid / LPT][tid % LPT] = nv;
+                store_new_chunk(a, nslot, g, tid / LPT, tid % LPT, nv);
+            }
         }
-        // Fused append: the workgroup holding the sequence's last block
-        // writes the step's new K/V row of this KV head to its slot, and
-        // keeps it in LDS so that the attention reads position L-1 from it
-        // rather than from the cache written in the same launch.
-        const int nslot = (a.k_new && j1 == nblk) ? a.slots[b] : -1;
         const bool fresh = (unsigned)nslot < (unsigned)(a.num_blocks * BS);
-        if (fresh && tid < 2 * LPT) {
-            const int kv = tid / LPT, i = tid % LPT;
-            const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
-                [((int64_t)b * a.Hkv + g) * LPT + i];
-            lds_new[kv][i] = row;
-            store_new_chunk(a, nslot, g, kv, i, row);
-        }
-        __syncthreads();
+        lds_barrier();
 
         // This lane's B operand of S = K Q^T: chunk 4 kk + g4 of query head
         // n's row (zero for the padding columns n >= G).
@@ -591,9 +621,11 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         // for it would drain the prefetch.
         for (; c0 < j1; c0 += kIdChunk) {
           const int c1 = j1 - c0 < kIdChunk ? j1 : c0 + kIdChunk;
-          for (int i = tid; i < c1 - c0; i += kThreads)
-              lds_ids[i] = bt[c0 + i];
-          __syncthreads();
+          if (c0 != j0) {                  // the first chunk came with the q rows
+              for (int i = tid; i < c1 - c0; i += kThreads)
+                  lds_ids[i] = bt[c0 + i];
+              lds_barrier();
+          }
           if (c0 + w < c1) {
             const int E = ((c1 - c0 - w + NW - 1) / NW) * NSUB;
             auto id_of = [&](int e) {
@@ -625,7 +657,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
                 idC = idn;
             }
           }
-          __syncthreads();
+          lds_barrier();
         }
 
         // Per head: the sum over the 4 quarters (m is already common to
@@ -648,7 +680,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
                 lds_l[w][n] = l;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // Merge the 4 waves; a sequence held whole by this range is final.
         const bool whole = owner(cost_at(sb, b, a.piece_cost), Ct, a.W) ==
@@ -683,7 +715,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         x = sb + j1;
         ++b;
     }
