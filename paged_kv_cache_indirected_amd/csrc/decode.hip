@@ -240,17 +240,24 @@ __device__ __forceinline__ bool empty_range(int w, int64_t Ct, int W)
     return Ct * w / W == Ct * (w + 1) / W;
 }
 
-// First flattened block whose cost is >= c (T if none).
-__device__ __forceinline__ int block_at_cost(const int32_t *pref, int B, int pc, int64_t c)
+// Number of sequences b < B for which pred(b) holds, pred being true on a
+// prefix of b: wave ballots, every wave alone (the result is uniform).
+template <typename P>
+__device__ __forceinline__ int count_prefix(int B, int lane, P pred)
 {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cost_at(pref[mid], mid, pc) <= c)
-            lo = mid;
-        else
-            hi = mid - 1;
+    int n = 0;
+    for (int base = 0; base < B; base += 64) {
+        const int b = base + lane;
+        n += __popcll(__ballot(b < B && pred(b)));
     }
+    return n;
+}
+
+// First flattened block whose cost is >= c (T if none).
+__device__ __forceinline__ int block_at_cost(const int32_t *pref, int B, int pc, int64_t c,
+                                             int lane)
+{
+    const int lo = count_prefix(B, lane, [&](int b) { return cost_at(pref[b], b, pc) <= c; }) - 1;
     const int64_t x = pref[lo] + (c - cost_at(pref[lo], lo, pc));
     return (int)(x < pref[lo + 1] ? x : pref[lo + 1]);
 }
@@ -408,35 +415,51 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     const int g4 = lane >> 4, n = lane & 15;
 
     // Prefix sums of the per-sequence block counts (the same in every
-    // workgroup).
-    int carry = 0;
-    for (int base = 0; base < a.B; base += kThreads) {
-        const int b = base + tid;
-        int v = b < a.B ? (clamp_len<BS>(a, b) + BS - 1) / BS : 0;
+    // workgroup).  Up to 64 sequences every wave computes them alone and
+    // writes the whole table itself, so it reads it back with no barrier
+    // (the other waves write the same values).
+    if (a.B <= 64) {
+        int v = lane < a.B ? (clamp_len<BS>(a, lane) + BS - 1) / BS : 0;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int t = __shfl_up(v, off);
             if (lane >= off)
                 v += t;
         }
-        if (lane == 63)
-            lds_wsum[w] = v;
-        lds_barrier();
-        int before = 0, tot = 0;
+        if (lane < a.B)
+            lds_pref[lane + 1] = v;
+        if (lane == 0)
+            lds_pref[0] = 0;
+    } else {
+        int carry = 0;
+        for (int base = 0; base < a.B; base += kThreads) {
+            const int b = base + tid;
+            int v = b < a.B ? (clamp_len<BS>(a, b) + BS - 1) / BS : 0;
 #pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const int s = lds_wsum[i];
-            before += i < w ? s : 0;
-            tot += s;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(v, off);
+                if (lane >= off)
+                    v += t;
+            }
+            if (lane == 63)
+                lds_wsum[w] = v;
+            lds_barrier();
+            int before = 0, tot = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const int s = lds_wsum[i];
+                before += i < w ? s : 0;
+                tot += s;
+            }
+            if (b < a.B)
+                lds_pref[b + 1] = carry + before + v;
+            carry += tot;
+            lds_barrier();
         }
-        if (b < a.B)
-            lds_pref[b + 1] = carry + before + v;
-        carry += tot;
+        if (tid == 0)
+            lds_pref[0] = 0;
         lds_barrier();
     }
-    if (tid == 0)
-        lds_pref[0] = 0;
-    lds_barrier();
     const int T = lds_pref[a.B];
     const int hq0 = g * G;
 
@@ -445,24 +468,13 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
             a.ws_pref[i] = lds_pref[i];
 
     const int64_t Ct = (int64_t)T + (int64_t)a.piece_cost * a.B;
-    const int64_t start = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * wg / a.W);
-    const int64_t end = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * (wg + 1) / a.W);
+    const int64_t start = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * wg / a.W, lane);
+    const int64_t end = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * (wg + 1) / a.W, lane);
     if (start >= end)
         return;
 
     // First sequence with blocks in the range: the last b with pref[b] <= start.
-    int b;
-    {
-        int lo = 0, hi = a.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (lds_pref[mid] <= start)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        b = lo;
-    }
+    int b = count_prefix(a.B, lane, [&](int s) { return lds_pref[s] <= start; }) - 1;
 
     const int64_t blk_bytes = (int64_t)a.Hkv * TILE;
     const char *kbase = static_cast<const char *>(a.kc) + (int64_t)g * TILE;
