@@ -163,7 +163,7 @@ def bench_probes(timer):
             "note": "contiguous read of 2 GiB, 2048 workgroups"}, lib, sink
 
 
-def bench_tile_probe(lib, sink, states, sh, kv_bytes, timer):
+def bench_tile_probe(lib, sink, states, sh, kv_bytes, timer, grid=256):
     """The decode's access shape without arithmetic: whole (block, head)
     tiles of K and V of the same shuffled pools, in sequence order."""
     import torch
@@ -186,7 +186,7 @@ def bench_tile_probe(lib, sink, states, sh, kv_bytes, timer):
         t = lists[i[0] % len(states)]
         i[0] += 1
         lib.pkv_probe_tile_read(s["cache"].k_cache.data_ptr(), s["cache"].v_cache.data_ptr(),
-                                t.data_ptr(), t.numel(), tile, sink.data_ptr(), 4096, st)
+                                t.data_ptr(), t.numel(), tile, sink.data_ptr(), grid, st)
     t = timer.per_call(run, 40)
     return round(kv_bytes / float(np.median(t)) / 1e9, 1)
 
@@ -829,7 +829,9 @@ def main():
         probes, plib, sink = bench_probes(timer)
         probes["paged_tile_read_GBps"] = bench_tile_probe(plib, sink, states, sh, kv_bytes, timer)
         probes["paged_tile_note"] = ("the decode's tiles of the same shuffled pools, read with "
-                                     "its access shape and no arithmetic")
+                                     "its access shape (one workgroup per CU, each wave a "
+                                     "contiguous run of the tile list, two tiles in flight) and "
+                                     "no arithmetic")
         res["roofline"]["achievable_probes"] = probes
         res["roofline"]["frac_of_paged_tile_probe"] = round(
             gbs_dec / probes["paged_tile_read_GBps"], 4)

@@ -5,8 +5,9 @@
 //                          achievable HBM read rate of this part.
 //   pkv_probe_tile_read    read whole (block, KV head) tiles of K and V
 //                          named by a list of tile indices, with the decode
-//                          kernel's access shape (one wave per tile, 16 bytes
-//                          per lane per load, 4 KiB contiguous per tile): the
+//                          kernel's access shape (each wave a contiguous run
+//                          of the list, 16 bytes per lane per load, 4 KiB
+//                          contiguous per tile, two tiles in flight): the
 //                          achievable rate of the paged gather itself, with
 //                          no arithmetic.
 //   pkv_probe_copy         copy n 16-byte chunks: a kernel of known traffic
@@ -44,22 +45,64 @@ __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4 *__restric
 }
 
 // tiles[i] = index of a (block, head) tile of tile_bytes in each of k and v.
-// Wave w of workgroup x takes tiles x * 4 + w, x * 4 + w + 4 * grid, ...
+// Wave v of the grid reads tiles [v * per, (v + 1) * per) of the list, in
+// order, as the decode's workgroups read their ranges: 64 tile indices are
+// fetched in one load (lane i holds the i-th) and read back with readlane,
+// so no data load waits on an index load; two tiles (both tensors) are in
+// flight at a time, 1 KiB per wave load.
 __global__ __launch_bounds__(kThreads) void k_tile_read(const char *__restrict__ kc,
                                                         const char *__restrict__ vc,
                                                         const int64_t *__restrict__ tiles,
                                                         int64_t ntiles, int tile_bytes,
                                                         uint32_t *__restrict__ sink)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+    const int64_t v = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t per = (ntiles + nwaves - 1) / nwaves;
+    const int64_t t0 = v * per;
+    const int64_t t1 = t0 + per < ntiles ? t0 + per : ntiles;
+    const int runs = tile_bytes / 1024;
     uint32_t acc = 0;
-    const int per = tile_bytes / 1024;
-    for (int64_t t = (int64_t)blockIdx.x * 4 + w; t < ntiles; t += (int64_t)gridDim.x * 4) {
-        const int64_t base = tiles[t] * tile_bytes + lane * 16;
-        for (int c = 0; c < per; ++c) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(kc + base + c * 1024);
-            const uint4 b = *reinterpret_cast<const uint4 *>(vc + base + c * 1024);
-            acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    for (int64_t base = t0; base < t1; base += 64) {
+        const int nt = (int)(t1 - base < 64 ? t1 - base : 64);
+        const int64_t my = lane < nt ? tiles[base + lane] : 0;
+        const uint32_t lo = (uint32_t)my, hi = (uint32_t)(my >> 32);
+        for (int j = 0; j < nt; j += 2) {
+            // A pair of tiles, or the last tile alone (the second tile's
+            // loads are then skipped).
+            const bool pair = j + 1 < nt;
+            const int64_t id0 = ((int64_t)__builtin_amdgcn_readlane(hi, j) << 32) |
+                                __builtin_amdgcn_readlane(lo, j);
+            const int jj = pair ? j + 1 : j;
+            const int64_t id1 = ((int64_t)__builtin_amdgcn_readlane(hi, jj) << 32) |
+                                __builtin_amdgcn_readlane(lo, jj);
+            const char *k0 = kc + id0 * tile_bytes + lane * 16, *v0 = vc + id0 * tile_bytes + lane * 16;
+            const char *k1 = kc + id1 * tile_bytes + lane * 16, *v1 = vc + id1 * tile_bytes + lane * 16;
+            for (int c = 0; c < runs; c += 4) {
+                uint4 r[16];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int cc = c + u < runs ? c + u : runs - 1;
+                    r[u] = *reinterpret_cast<const uint4 *>(k0 + cc * 1024);
+                    r[4 + u] = *reinterpret_cast<const uint4 *>(v0 + cc * 1024);
+                }
+                if (pair) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int cc = c + u < runs ? c + u : runs - 1;
+                        r[8 + u] = *reinterpret_cast<const uint4 *>(k1 + cc * 1024);
+                        r[12 + u] = *reinterpret_cast<const uint4 *>(v1 + cc * 1024);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 8; u < 16; ++u)
+                        r[u] = make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+            }
         }
     }
     __shared__ uint32_t red[kThreads];
