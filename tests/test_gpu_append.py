@@ -90,6 +90,56 @@ def test_negative_and_out_of_range_slots_write_nothing():
     assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
 
 
+def _mixed_slots(g, nslots, T):
+    """T slot entries: runs of consecutive slots (random start, so some are
+    4-aligned at a 4-aligned row and some are not), lone random slots and -1
+    padding, all distinct."""
+    used, out = set(), []
+    while len(out) < T:
+        kind = g.integers(0, 4)
+        if kind == 0:
+            out.extend([-1] * int(g.integers(1, 4)))
+            continue
+        n = 1 if kind == 1 else int(g.integers(2, 41))
+        s0 = int(g.integers(0, nslots - n))
+        run = list(range(s0, s0 + n))
+        if any(x in used for x in run):
+            continue
+        used.update(run)
+        out.extend(run)
+    return np.array(out[:T], dtype=np.int32)
+
+
+@pytest.mark.parametrize("dtype,D,bs", [("bf16", 128, 16), ("bf16", 128, 32), ("bf16", 64, 16),
+                                        ("f32", 128, 16), ("f32", 64, 32)])
+def test_run_groups_and_row_groups_mixed(dtype, D, bs):
+    """Groups of 4 rows whose slots are 4 consecutive, 4-aligned slots take
+    the whole-group path; every other group (misaligned or broken runs,
+    padding, the ragged last group) goes row by row.  Both must equal the
+    oracle's slot writes over the whole image."""
+    nb, H, T = 48, 2, 203
+    g = np.random.default_rng([7, D, bs, len(dtype)])
+    slots = _mixed_slots(g, nb * bs, T)
+    say(f"[append mixed] {dtype} D={D} bs={bs} T={T} runs+rows")
+    dt_np = np.int32 if dtype == "f32" else np.int16
+    k = g.integers(-2**15, 2**15, size=(T, H, D)).astype(dt_np)
+    v = g.integers(-2**15, 2**15, size=(T, H, D)).astype(dt_np)
+    cache = PagedCache(nb, H, bs, D, DT[dtype])
+    kd = torch.from_numpy(k.view(np.float32) if dtype == "f32" else k).cuda()
+    vd = torch.from_numpy(v.view(np.float32) if dtype == "f32" else v).cuda()
+    if dtype == "bf16":
+        kd, vd = kd.view(torch.bfloat16), vd.view(torch.bfloat16)
+    pkv.append(kd, vd, torch.from_numpy(slots).cuda(), cache.k_cache, cache.v_cache, cache.desc)
+    torch.cuda.synchronize()
+    kc, vc = _image(cache)
+    pois = synth.POISON_F32 if dtype == "f32" else synth.POISON_BF16
+    ek = np.full(kc.shape, np.array(pois).astype(np.uint32 if dtype == "f32" else np.uint16)
+                 .view(dt_np), dtype=dt_np)
+    ev = ek.copy()
+    oracle.append(k, v, slots, ek, ev, bs)
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
+
+
 def test_append_is_idempotent_and_overwrites():
     cache = PagedCache(4, 1, 16, 64, pkv.F32)
     g = np.random.default_rng(1)
