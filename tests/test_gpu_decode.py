@@ -139,6 +139,29 @@ def test_batch_above_one_launch():
     assert max_err(out, ref) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("B", [63, 64, 65, 257])
+def test_batch_sizes_around_the_wave_width(B):
+    # The block prefix sums are computed by each wave alone up to 64
+    # sequences and by the whole workgroup above: both sides of the switch,
+    # with empty sequences among them.
+    g = np.random.default_rng([17, B])
+    lens = g.integers(1, 200, size=B)
+    b = synth.custom_decode(17 + B, lens, Hq=16, Hkv=2, D=128, dtype="bf16", block_size=16)
+    cache, q, tab, lens_d, mx = decode_state(b)
+    empty = [i for i in range(B) if i % 9 == 4]
+    for i in empty:
+        lens_d[i] = 0
+    out = run_decode(cache, q, tab, lens_d, mx, b.shape.scale)
+    for i in empty:
+        assert torch.count_nonzero(out[i]) == 0
+    keep = [i for i in range(B) if i % 9 != 4]
+    st = b.seq_start()
+    kk = np.concatenate([b.k[st[i]:st[i + 1]] for i in keep])
+    vv = np.concatenate([b.v[st[i]:st[i + 1]] for i in keep])
+    ref = oracle.decode(b.q[keep], kk, vv, b.lens[keep], b.shape.scale)
+    assert max_err(out[keep], ref) <= TOL["bf16"]
+
+
 def test_length_one_returns_v_exactly():
     for dtype in ("f32", "bf16"):
         b = synth.custom_decode(9, [1, 1, 1], Hq=16, Hkv=2, D=128, dtype=dtype, block_size=16)
