@@ -431,21 +431,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
                     o[dt][ct] *= alpha[ct];
         }
 
-        // O^T += V^T P^T (hi and lo parts).
+        // O^T += V^T P^T (hi and lo parts).  Each accumulator takes its hi
+        // product, then its lo product; the lo products of dims tile dt - 1
+        // are issued after the hi products of tile dt, so no MFMA waits for
+        // the one just before it to finish accumulating.
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
+        for (int s2 = 0; s2 < 2; ++s2) {
+            auto vload = [&](int dt) {
+                return *reinterpret_cast<const bf16x8 *>(
                     &lds_v[buf][(dt * 16 + n) * VSTR + vcol(dt * 16 + n, 32 * s2 + 8 * quad)]);
+            };
+            bf16x8 vprev = vload(0);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct][s2], o[dt][ct],
-                                                                        0, 0, 0);
-                    o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[ct][s2], o[dt][ct],
-                                                                        0, 0, 0);
-                }
+            for (int ct = 0; ct < 2; ++ct)
+                o[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vprev, phi[ct][s2], o[0][ct],
+                                                                   0, 0, 0);
+#pragma unroll
+            for (int dt = 1; dt < NDT; ++dt) {
+                const bf16x8 va = vload(dt);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct][s2],
+                                                                        o[dt][ct], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    o[dt - 1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        vprev, plo[ct][s2], o[dt - 1][ct], 0, 0, 0);
+                vprev = va;
             }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                o[NDT - 1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    vprev, plo[ct][s2], o[NDT - 1][ct], 0, 0, 0);
+        }
 
         if (kt + 1 < NT)
             store_tile(buf ^ 1);
