@@ -77,9 +77,13 @@ int pkv_abi_version(void);
  *
  *   k, v          [num_tokens][num_kv_heads][head_dim], cache dtype
  *   slot_mapping  [num_tokens] int32; row t goes to slot slot_mapping[t];
- *                 a negative slot skips the row.  Slots must be distinct.
+ *                 a negative slot, or one at or past num_blocks * block_size,
+ *                 skips the row.  Slots must be distinct.
  *   k_cache, v_cache  the caches described by `c`
- * Copies bits; no conversion.  num_tokens == 0 is a no-op.
+ * Copies bits; no conversion.  num_tokens == 0 is a no-op.  Rows 4t .. 4t+3
+ * mapped to 4 consecutive slots starting at a multiple of 4 (the rows of a
+ * prompt or a prefill chunk) are written as whole cache lines; other rows
+ * one by one.
  */
 int pkv_append(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
                void *k_cache, void *v_cache, const pkv_cache_desc *c, void *stream);
