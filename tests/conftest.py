@@ -13,8 +13,8 @@ _ORACLE = os.path.join(ROOT, "oracle", "liboracle.so")
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    # Build what is missing (never rebuild what exists: the GPU machine runs the
-    # libraries built in this tree).
+    # Build what is missing; never rebuild what exists, so the tests run the
+    # libraries already built in this tree.
     if not os.path.exists(_ORACLE):
         import oracle
         oracle.build()
