@@ -102,6 +102,22 @@ def workspace(B, Hq, max_len, desc, splits):
     return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
 
 
+class PrefillWorkspace:
+    """The workspace pkv_prefill_chunk asks for (key-split states), grown on
+    demand; a larger buffer than a call needs is fine."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, S, Hq, max_query_len, desc):
+        import torch
+        import paged_kv_cache_indirected_amd as pkv
+        n = pkv.prefill_workspace_bytes(S, Hq, max_query_len, desc)
+        if n and (self.buf is None or self.buf.numel() < n):
+            self.buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+        return self.buf if n else None
+
+
 def cpu_baseline(batch, min_seconds: float = 10.0, max_reps: int = 400):
     """The fp64 oracle on the same workload, all host cores, timed around the
     compute only.  The sample is the whole decode step, repeated until at
@@ -324,10 +340,11 @@ def bench_cfg5(timer, splits):
     dc = ds["cache"]
     ws = workspace(dec.B, sh.Hq, ds["max_len"], dc.desc, splits)
     C = int(pre.chunk.max())
+    pws = PrefillWorkspace().get(len(pre.chunk), sh.Hq, C, pc.desc)
 
     def prefill():
         pkv.prefill_chunk(pq, qsl, pc.k_cache, pc.v_cache, ptab, plens, sh.scale, pout, pc.desc,
-                          C, pmx)
+                          C, pmx, workspace=pws)
 
     def decode():
         pkv.decode(ds["q"], dc.k_cache, dc.v_cache, ds["tables"], ds["lens"], sh.scale, dout,
@@ -379,7 +396,41 @@ def bench_cfg5(timer, splits):
                          "one stream",
             "step_two_streams_ms": round(1e3 * t_step2, 4),
             "step_two_streams_note": "prefill (with its append) on the launch stream, decode "
-                                     "(with its append) on a second stream, joined by events"}
+                                     "(with its append) on a second stream, joined by events",
+            "short_chunk": bench_short_chunk(timer)}
+
+
+def bench_short_chunk(timer):
+    """One sequence prefilling a 64-token chunk over 8000 prior tokens
+    (64q/8kv, d128, bf16, block 16): 32 workgroups, far fewer than the CUs.
+    Timed as one pass per workgroup (no workspace) and with the keys split
+    (the workspace pkv_prefill_chunk asks for)."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    import synth
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    b = synth.custom_prefill(9001, prior=[8000], chunk=[64], Hq=64, Hkv=8, D=128, block_size=16)
+    sh = b.shape
+    cache = PagedCache(b.pool_blocks, sh.Hkv, sh.block_size, sh.D, pkv.BF16,
+                       pool_seed=b.pool_seed)
+    cache.add_sequences([0], b.lens, b.k, b.v)
+    tab, lens, mx = cache.tables([0])
+    q = to_device_rows(b.q, pkv.BF16, "cuda")
+    qs = torch.tensor([0, 64], dtype=torch.int32, device="cuda")
+    out = torch.empty(tuple(q.shape), dtype=torch.float32, device="cuda")
+    ws = PrefillWorkspace().get(1, sh.Hq, 64, cache.desc)
+
+    def run(w):
+        return lambda: pkv.prefill_chunk(q, qs, cache.k_cache, cache.v_cache, tab, lens,
+                                         sh.scale, out, cache.desc, 64, mx, workspace=w)
+    t1 = float(np.median(timer.per_call(run(None), 30)))
+    t2 = float(np.median(timer.per_call(run(ws), 30)))
+    flops = 4.0 * sh.Hq * sh.D * (64 * 8000 + 64 * 65 / 2)
+    return {"workload": "one 64-token chunk over 8000 prior tokens, 64q/8kv, d128, bf16",
+            "single_pass_ms": round(1e3 * t1, 4),
+            "key_split_ms": round(1e3 * t2, 4),
+            "key_split_TFLOPs": round(flops / t2 / 1e12, 1),
+            "speedup": round(t1 / t2, 3)}
 
 
 def bench_append(timer):
@@ -500,18 +551,20 @@ def bench_prefix_ttft(timer):
     slots_b = torch.tensor(np.array([bb[p // bs] * bs + p % bs for p in range(reused, total)],
                                     dtype=np.int32), device="cuda")
 
+    pws = PrefillWorkspace().get(1, Hq, C, cache.desc)
+
     def cold():
         for i in range(total // C):
             lo = i * C
             pkv.append(dk[lo:lo + C], dv[lo:lo + C], slots_a[lo:lo + C], cache.k_cache,
                        cache.v_cache, cache.desc)
             pkv.prefill_chunk(dq, qs, cache.k_cache, cache.v_cache, tab_a, lens_chunks[i],
-                              scale, out, cache.desc, C, C * (i + 1))
+                              scale, out, cache.desc, C, C * (i + 1), workspace=pws)
 
     def warm():
         pkv.append(dk[reused:], dv[reused:], slots_b, cache.k_cache, cache.v_cache, cache.desc)
         pkv.prefill_chunk(dq, qs, cache.k_cache, cache.v_cache, tab_b, lens_b, scale, out,
-                          cache.desc, C, mx_b)
+                          cache.desc, C, mx_b, workspace=pws)
     t_cold = float(np.median(timer.per_call(cold, 10)))
     t_warm = float(np.median(timer.per_call(warm, 10)))
     return {"workload": "prefix cache TTFT proxy: one 2560-token prompt (2048-token shared "
@@ -552,6 +605,7 @@ def bench_sched(steps=300, warm=60):
                          device="cuda")
         pout = torch.empty((budget, Hq, D), dtype=torch.float32, device="cuda")
         dout = torch.empty((64, Hq, D), dtype=torch.float32, device="cuda")
+        pwsp = PrefillWorkspace()
         step_ms, arrive, ttft, clock, decoded, nreq = [], {}, [], 0.0, 0, 0
         for st in range(steps):
             for _ in range(int(arrivals[st])):
@@ -570,13 +624,16 @@ def bench_sched(steps=300, warm=60):
             if len(p["decode_ids"]):
                 dtab, dlens, dmx = cache.tables(list(p["decode_ids"]))
             sl = torch.from_numpy(slots).cuda()
+            pws = (pwsp.get(len(p["chunk_ids"]), Hq, int(p["chunk_len"].max()), cache.desc)
+                   if len(p["chunk_ids"]) else None)
             e0.record()
             if n:
                 pkv.append(rows[:n], rows[:n], sl, cache.k_cache, cache.v_cache, cache.desc)
             if len(p["chunk_ids"]):
                 T = int(p["chunk_len"].sum())
                 pkv.prefill_chunk(qrows[:T], qs, cache.k_cache, cache.v_cache, ptab, plens, scale,
-                                  pout[:T], cache.desc, int(p["chunk_len"].max()), pmx)
+                                  pout[:T], cache.desc, int(p["chunk_len"].max()), pmx,
+                                  workspace=pws)
             if len(p["decode_ids"]):
                 B = len(p["decode_ids"])
                 pkv.decode(qrows[:B], cache.k_cache, cache.v_cache, dtab, dlens, scale, dout[:B],

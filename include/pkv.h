@@ -227,7 +227,17 @@ int pkv_decode_cascade(const void *q, const void *k_cache, const void *v_cache,
  *   query_start_loc  [num_seqs + 1] int32, non-decreasing, starts at 0
  *   max_query_len    host-side upper bound of C_b
  *   out              like q, out_dtype PKV_F32 or PKV_BF16
- *   workspace        may be NULL when pkv_prefill_workspace_bytes(...) is 0
+ *   workspace        caller-owned device memory of workspace_bytes bytes, no
+ *                    initialisation needed; may be NULL.
+ * Key splits.  When the grid (num_kv_heads x num_seqs x q-tiles workgroups)
+ * has fewer workgroups than the device has compute units (a short chunk of
+ * one or a few sequences), the keys of each workgroup are split k ways; every split writes an fp32 state (normalised output and
+ * log2-sum-exp) into the workspace and a log-sum-exp merge writes out.  The
+ * result equals the single pass up to fp32 rounding order.
+ * pkv_prefill_workspace_bytes gives the bytes for the largest split the
+ * library would choose for these sizes (0: it would not split); a NULL or
+ * shorter workspace makes it split less or not at all.  Calls sharing a
+ * workspace must not overlap.
  * Supported: dtype BF16 only (PKV_EUNSUPPORTED for F32), head_dim 64/128,
  * block_size 16/32, G in {1, 2, 4, 8}.
  */

@@ -1,6 +1,7 @@
 // C ABI entry points of libpkv: argument validation, launch geometry and
 // workspace sizing.  Every step of the computation runs in the HIP kernels;
 // this file only checks host scalars and pointers and picks launch shapes.
+#include <algorithm>
 #include <cmath>
 
 #include "pkv_internal.h"
@@ -90,6 +91,48 @@ WsLayout ws_layout(int32_t B, int32_t hq, int32_t W, int32_t D)
     l.o = align256((bc + 1) * sizeof(int32_t));
     l.ml = l.o + align256(pieces * hq * D * sizeof(float));
     l.total = l.ml + pieces * hq * 2 * sizeof(float);
+    return l;
+}
+
+// Key splits of a chunked prefill.  The grid has Hkv * S * q-tiles
+// workgroups; when that is fewer than the device's CUs (a short chunk of one
+// or a few sequences), CUs sit idle for the whole call.  Splitting each
+// workgroup's keys k ways (each split writes an fp32 state and its
+// log2-sum-exp, merged afterwards) gives about one workgroup per CU, keeping
+// at least 8 key tiles of 64 per split.  Larger grids are not split: a CU
+// left with one workgroup in a partly full last round runs it about twice as
+// fast, so the tail costs less than the states' traffic and the merge.
+// max_ctx < 0: no bound from the context (the workspace size query).
+int32_t prefill_key_splits(int32_t S, int32_t hq, int32_t maxq, int64_t max_ctx,
+                           const pkv_cache_desc *c)
+{
+    if (S <= 0 || maxq <= 0 || hq <= 0 || !c || c->num_kv_heads <= 0)
+        return 1;
+    const int64_t tq = pkv::prefill_rows_per_workgroup() / (hq / c->num_kv_heads);
+    const int64_t nqt = (maxq + tq - 1) / tq;
+    const int64_t items = (int64_t)c->num_kv_heads * S * nqt;
+    int64_t ks = (int64_t)pkv::device_cu_count() / items;
+    if (max_ctx >= 0)
+        ks = std::min<int64_t>(ks, (max_ctx + 63) / 64 / 8);
+    ks = std::min<int64_t>(ks, 16);
+    ks = std::min<int64_t>(ks, 65535 / std::max<int64_t>(nqt, 1));
+    return (int32_t)std::max<int64_t>(ks, 1);
+}
+
+// Prefill split states: fp32 outputs [ks][S * maxq * Hq][D], then
+// log2-sum-exp [ks][S * maxq * Hq].
+struct PrefillWs {
+    int64_t rows;
+    size_t o, lse, total;
+};
+
+PrefillWs prefill_layout(int32_t S, int32_t hq, int32_t maxq, int32_t D, int32_t ks)
+{
+    PrefillWs l;
+    l.rows = (int64_t)S * maxq * hq;
+    l.o = 0;
+    l.lse = align256((size_t)ks * l.rows * D * sizeof(float));
+    l.total = l.lse + align256((size_t)ks * l.rows * sizeof(float));
     return l;
 }
 
@@ -261,7 +304,7 @@ int32_t cascade_splits(int32_t B, int32_t hq, int32_t nb, const pkv_cache_desc *
 {
     if (nb <= 0 || B <= 0)
         return 0;
-    const int64_t tq = 128 / (hq / c->num_kv_heads);          // query tokens per prefill tile
+    const int64_t tq = pkv::prefill_rows_per_workgroup() / (hq / c->num_kv_heads);  // tokens per prefill tile
     const int64_t per = (int64_t)c->num_kv_heads * ((B + tq - 1) / tq);
     int64_t ks = (pkv::device_cu_count() + per - 1) / per;
     ks = ks < 1 ? 1 : (ks > nb ? nb : ks);
@@ -410,11 +453,13 @@ extern "C" int pkv_decode_cascade(const void *q, const void *k_cache, const void
 extern "C" size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t max_query_len, const pkv_cache_desc *c)
 {
-    (void)num_seqs;
-    (void)num_q_heads;
-    (void)max_query_len;
-    (void)c;
-    return 0;
+    if (!c || c->dtype != PKV_BF16 || c->num_kv_heads <= 0 || num_q_heads <= 0 ||
+        num_q_heads % c->num_kv_heads || (c->head_dim != 64 && c->head_dim != 128))
+        return 0;
+    const int32_t ks = prefill_key_splits(num_seqs, num_q_heads, max_query_len, -1, c);
+    if (ks <= 1)
+        return 0;
+    return prefill_layout(num_seqs, num_q_heads, max_query_len, c->head_dim, ks).total;
 }
 
 extern "C" int pkv_prefill_chunk(const void *q, const int32_t *query_start_loc, int32_t num_seqs,
@@ -426,8 +471,6 @@ extern "C" int pkv_prefill_chunk(const void *q, const int32_t *query_start_loc, 
                                  void *stream)
 {
     static const char *who = "pkv_prefill_chunk";
-    (void)workspace;
-    (void)workspace_bytes;
     pkv::clear_error();
     int rc = check_desc(c, who);
     if (rc || (rc = check_heads(num_q_heads, c, who)))
@@ -455,5 +498,29 @@ extern "C" int pkv_prefill_chunk(const void *q, const int32_t *query_start_loc, 
                          block_tables, block_table_stride, context_lens, max_context_len,
                          num_q_heads, c->num_kv_heads, c->num_blocks, c->block_size, c->head_dim,
                          scale, out, out_dtype, stream};
-    return pkv::launch_prefill(p);
+    // Key splits when the workspace holds their states (fewer if it is
+    // short; none without one).
+    int32_t ks = workspace ? prefill_key_splits(num_seqs, num_q_heads, max_query_len,
+                                                max_context_len, c)
+                           : 1;
+    while (ks > 1 &&
+           prefill_layout(num_seqs, num_q_heads, max_query_len, c->head_dim, ks).total >
+               workspace_bytes)
+        --ks;
+    if (ks <= 1)
+        return pkv::launch_prefill(p);
+    if ((rc = check_ptr(workspace, "workspace", who)))
+        return rc;
+    const PrefillWs lay = prefill_layout(num_seqs, num_q_heads, max_query_len, c->head_dim, ks);
+    float *so = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.o);
+    float *sl = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.lse);
+    p.out = so;
+    p.out_dtype = PKV_F32;
+    p.lse = sl;
+    p.key_splits = ks;
+    p.split_rows = lay.rows;
+    if ((rc = pkv::launch_prefill(p)))
+        return rc;
+    return pkv::launch_merge_states(so, sl, ks, lay.rows, c->head_dim, out, out_dtype, stream,
+                                    query_start_loc + num_seqs, num_q_heads);
 }

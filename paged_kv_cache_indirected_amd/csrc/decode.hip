@@ -816,10 +816,13 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
 template <int D>
 __global__ __launch_bounds__(D) void k_merge_states(const float *__restrict__ o,
                                                     const float *__restrict__ lse, int32_t K,
-                                                    int64_t rows, void *out, int32_t out_dtype)
+                                                    int64_t rows, void *out, int32_t out_dtype,
+                                                    const int32_t *row_tokens, int32_t heads)
 {
     const int64_t r = blockIdx.x;
     const int d = threadIdx.x;
+    if (row_tokens && r >= (int64_t)row_tokens[0] * heads)
+        return;
     float M = -INFINITY;
     for (int k = 0; k < K; ++k)
         M = fmaxf(M, lse[k * rows + r]);
@@ -981,7 +984,8 @@ int launch_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int3
 }
 
 int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t rows,
-                        int32_t head_dim, void *out, int32_t out_dtype, void *stream)
+                        int32_t head_dim, void *out, int32_t out_dtype, void *stream,
+                        const int32_t *row_tokens, int32_t heads)
 {
     if (rows == 0)
         return PKV_OK;
@@ -990,10 +994,10 @@ int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t row
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 64)
         hipLaunchKernelGGL(k_merge_states<64>, dim3((unsigned)rows), dim3(64), 0, st, o, lse, k,
-                           rows, out, out_dtype);
+                           rows, out, out_dtype, row_tokens, heads);
     else
         hipLaunchKernelGGL(k_merge_states<128>, dim3((unsigned)rows), dim3(128), 0, st, o, lse, k,
-                           rows, out, out_dtype);
+                           rows, out, out_dtype, row_tokens, heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(PKV_EHIP, "state merge launch failed: %s", hipGetErrorString(e));

@@ -53,9 +53,12 @@ int launch_decode(const DecodeLaunch &a);
 // Cost of a sequence boundary in a decode workgroup's range, in blocks.
 int32_t decode_piece_cost(int32_t block_size, int32_t head_dim, int32_t elem_size);
 // out[r][d] = sum_k o[k][r][d] 2^(lse[k][r] - M) / sum_k 2^(lse[k][r] - M),
-// M = max_k lse[k][r] (zeros where every state is empty), r < rows.
+// M = max_k lse[k][r] (zeros where every state is empty), r < rows; with
+// row_tokens set, only rows r < row_tokens[0] * heads are merged (the rest of
+// the states' rows are padding and out holds no such rows).
 int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t rows,
-                        int32_t head_dim, void *out, int32_t out_dtype, void *stream);
+                        int32_t head_dim, void *out, int32_t out_dtype, void *stream,
+                        const int32_t *row_tokens = nullptr, int32_t heads = 0);
 // qs[k] = k B (k <= ks), lens[k] = min(nbk, nb - k nbk) bs (k < ks).
 int launch_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int32_t nbk,
                          int32_t nb, int32_t bs, void *stream);
@@ -116,7 +119,11 @@ struct PrefillLaunch {
     int32_t causal = 1;        // 0: every row attends all keys of its sequence
     int32_t q_shared = 0;      // 1: every sequence reads queries from rows 0..C-1
     float *lse = nullptr;      // optional [rows][Hq] log2-sum-exp of the scaled scores
+    int32_t key_splits = 1;    // > 1: split k writes its fp32 state at out + k * split_rows * D
+    int64_t split_rows = 0;    //      and its log2-sum-exp at lse + k * split_rows
 };
 int launch_prefill(const PrefillLaunch &a);
+// Query rows (GQA-packed (token, head) pairs) one prefill workgroup holds.
+int32_t prefill_rows_per_workgroup();
 
 }  // namespace pkv

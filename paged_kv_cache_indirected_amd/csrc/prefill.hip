@@ -12,8 +12,10 @@
 // Design (one workgroup = 128 GQA-packed query rows of one (sequence, KV
 // head); row r is chunk token r / G, query head g*G + r % G, so every K/V
 // tile staged once serves all G heads of the group):
-//   * 4 waves x 32 rows.  Keys are processed in tiles of 64.  The workgroup
-//     stages each tile of K ([64][D], row-major) and V (transposed, [D][64],
+//   * 4 waves x 32 rows (NCT = 2 column tiles of 16; 48 rows per wave need
+//     more than half the register file, and one wave per SIMD ran 1.6x
+//     slower).  Keys are processed in tiles of 64.  The workgroup stages
+//     each tile of K ([64][D], row-major) and V (transposed, [D][64],
 //     keys in the MFMA k order) into LDS from the paged cache with coalesced
 //     16-byte loads (1 KiB runs of a block's tile; the cache's V tiles
 //     already hold 4 consecutive keys of a dim together), double buffered:
@@ -52,7 +54,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int NW = 4;                  // waves per workgroup
 constexpr int kThreads = NW * 64;
 constexpr int KT = 64;                 // keys per tile
-constexpr int ROWS = NW * 32;          // query rows per workgroup (32 per wave)
+constexpr int NCT = 2;                 // 16-column MFMA tiles per wave
+constexpr int WROWS = 16 * NCT;        // query rows per wave
+constexpr int ROWS = NW * WROWS;       // query rows per workgroup
 constexpr float kLazyMax = 8.0f;       // running-max slack, log2 units
 constexpr int kIdChunk = 1024;         // block ids staged in LDS at a time
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data format, no swizzle
@@ -85,6 +89,8 @@ struct PArgs {
     int32_t q_shared;                 // 1: every sequence reads its queries from rows 0..C-1
     float *lse;                       // optional [rows][Hq]: log2-sum-exp of the scaled scores
     float scale_log2;
+    int32_t ks;                       // key splits: split k writes state k (fp32 out + lse)
+    int64_t split_rows;               // rows of one split's state (out / lse stride)
 };
 
 // LDS column of key kk (0..63) in the transposed V tile: the 8 keys a lane
@@ -133,7 +139,7 @@ __device__ __forceinline__ float xsum(float v)
 }
 
 template <int D, int BS, int G>
-__global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
+__global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
 {
     using Sh = PShape<D>;
     constexpr int TQ = ROWS / G;                     // chunk tokens per workgroup
@@ -147,7 +153,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     __shared__ int32_t lds_ids[IDS];
 
     const int g = blockIdx.x;
-    const int qt = a.n_qtiles - 1 - (int)blockIdx.y;
+    const int qt = a.n_qtiles - 1 - (int)blockIdx.y / a.ks;
+    const int ksp = (int)blockIdx.y % a.ks;          // key split of this workgroup
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, quad = lane >> 4;
@@ -180,15 +187,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     const int tok_end = min(C, tok0 + TQ);
     const int kend = a.causal ? min(L, p0 + tok_end) : L;   // keys any row of this tile attends
     const int NT = kend > 0 ? (kend + KT - 1) / KT : 0;
+    // Key split ksp takes tiles [t0, t1) of the NT; an empty split still
+    // writes its (zero, -inf) state.
+    const int t0 = (int)((int64_t)NT * ksp / a.ks);
+    const int t1 = (int)((int64_t)NT * (ksp + 1) / a.ks);
 
     // This lane's two query columns (one per 16-row MFMA tile).
-    int lim[2];
-    bool valid[2];
-    int64_t qrow[2], qin[2];
+    int lim[NCT];
+    bool valid[NCT];
+    int64_t qrow[NCT], qin[NCT];
     const int qbase = a.q_shared ? 0 : q0;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const int r = w * 32 + ct * 16 + n;
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int r = w * WROWS + ct * 16 + n;
         const int tok = tok0 + r / G;
         valid[ct] = tok < tok_end;
         lim[ct] = valid[ct] ? (a.causal ? p0 + tok : L - 1) : -1;
@@ -197,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     }
     // Smallest key limit over the wave's valid rows (wave-uniform): a tile
     // entirely at or below it needs no mask.
-    const int wtok = tok0 + (w * 32) / G;
+    const int wtok = tok0 + (w * WROWS) / G;
     const int lim_w = wtok < tok_end ? (a.causal ? p0 + wtok : L - 1) : 0x7FFFFFFF;
 
     // Scores enter the exponent as fma(s, c, -m) with c = |scale| log2(e):
@@ -206,9 +217,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
     // (c is kept away from 0 so that masked -inf scores still give 0.)
     const float c = fmaxf(a.scale_log2 < 0.0f ? -a.scale_log2 : a.scale_log2, 1e-30f);
     const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
-    bf16x8 qf[2][NDS];
+    bf16x8 qf[NCT][NDS];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
             uint4 v = make_uint4(0, 0, 0, 0);
@@ -309,25 +320,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
         }
     };
 
-    f32x4 o[NDT][2];
+    f32x4 o[NDT][NCT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
             o[dt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+    float m[NCT], lsum[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        m[ct] = -INFINITY;
+        lsum[ct] = 0.0f;
+    }
 
-    if (NT > 0) {
-        stage_ids(0);
+    if (t1 > t0) {
+        stage_ids(t0 / CT);
         __syncthreads();
-        load_tile(0);
+        load_tile(t0);
         store_tile(0);
     }
     __syncthreads();
 
-    for (int kt = 0; kt < NT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < NT) {
+    for (int kt = t0; kt < t1; ++kt) {
+        const int buf = (kt - t0) & 1;
+        if (kt + 1 < t1) {
             if ((kt + 1) % CT == 0) {                // next tile starts a new id chunk
                 stage_ids((kt + 1) / CT);
                 __syncthreads();
@@ -336,11 +352,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
         }
 
         // S^T tile: 64 keys x 32 query columns.
-        f32x4 sacc[4][2];
+        f32x4 sacc[4][NCT];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
                 sacc[ks][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds)
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
                 const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
                     &lds_k[buf][(ks * 16 + n) * KSTR + ds * 32 + quad * 8]);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
                     sacc[ks][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ct][ds],
                                                                            sacc[ks][ct], 0, 0, 0);
             }
@@ -361,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
         const bool full = kt * KT + KT - 1 <= lim_w;
         if (!full) [[unlikely]] {
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -369,11 +385,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
                         if (kt * KT + ks * 16 + quad * 4 + i > lim[ct])
                             sacc[ks][ct][i] = -INFINITY;
         }
-        bf16x8 phi[2][2], plo[2][2];
+        bf16x8 phi[NCT][2], plo[NCT][2];
         bool grew = false;
-        float alpha[2];
+        float alpha[NCT];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             float mt = -INFINITY;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
@@ -427,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
                     o[dt][ct] *= alpha[ct];
         }
 
@@ -443,55 +459,62 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PArgs a)
             };
             bf16x8 vprev = vload(0);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
                 o[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vprev, phi[ct][s2], o[0][ct],
                                                                    0, 0, 0);
 #pragma unroll
             for (int dt = 1; dt < NDT; ++dt) {
                 const bf16x8 va = vload(dt);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
                     o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct][s2],
                                                                         o[dt][ct], 0, 0, 0);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
                     o[dt - 1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         vprev, plo[ct][s2], o[dt - 1][ct], 0, 0, 0);
                 vprev = va;
             }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
                 o[NDT - 1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     vprev, plo[ct][s2], o[NDT - 1][ct], 0, 0, 0);
         }
 
-        if (kt + 1 < NT)
+        if (kt + 1 < t1)
             store_tile(buf ^ 1);
         __syncthreads();
     }
 
     // Normalise and write: lane holds O^T[dt*16 + 4*quad + i][column n].
+    // With key splits the output is split ksp's fp32 state.
+    float *const lse_out = a.lse ? a.lse + ksp * a.split_rows : nullptr;
+    void *const out = a.ks > 1 ? static_cast<void *>(static_cast<float *>(a.out) +
+                                                     ksp * a.split_rows * D)
+                               : a.out;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
         float l = lsum[ct];
         l = xsum<16>(l);
         l = xsum<32>(l);
-        if (!valid[ct])
+        // (A split's state has S * max_query_len rows: rows past that exist
+        // only if a chunk exceeds max_query_len, and are not written.)
+        if (!valid[ct] || (a.ks > 1 && qrow[ct] / D >= a.split_rows))
             continue;
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        if (a.lse && quad == 0)
-            a.lse[qrow[ct] / D] = l > 0.0f ? m[ct] + __log2f(l) : -INFINITY;
+        if (lse_out && quad == 0)
+            lse_out[qrow[ct] / D] = l > 0.0f ? m[ct] + __log2f(l) : -INFINITY;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const int64_t idx = qrow[ct] + dt * 16 + quad * 4;
             const f32x4 r = o[dt][ct] * inv;
             if (a.out_dtype == PKV_F32) {
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + idx) = r;
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + idx) = r;
             } else {
                 uint2 pk;
                 pk.x = (uint32_t)bf16_rne(r[0]) | ((uint32_t)bf16_rne(r[1]) << 16);
                 pk.y = (uint32_t)bf16_rne(r[2]) | ((uint32_t)bf16_rne(r[3]) << 16);
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + idx) = pk;
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + idx) = pk;
             }
         }
     }
@@ -520,6 +543,8 @@ KernelFn pick(int D, int BS, int G)
 
 }  // namespace
 
+int32_t prefill_rows_per_workgroup() { return ROWS; }
+
 int launch_prefill(const PrefillLaunch &p)
 {
     if (p.num_seqs == 0 || p.max_query_len == 0)
@@ -531,9 +556,12 @@ int launch_prefill(const PrefillLaunch &p)
                     "group %d", p.head_dim, p.block_size, G);
     const int tq = ROWS / G;
     const int64_t nqt = ((int64_t)p.max_query_len + tq - 1) / tq;
-    if (nqt > 65535)
-        return fail(PKV_EINVAL, "pkv_prefill_chunk: max_query_len %d needs %lld q-tiles",
-                    p.max_query_len, (long long)nqt);
+    const int ks = p.key_splits < 1 ? 1 : p.key_splits;
+    if (nqt * ks > 65535)
+        return fail(PKV_EINVAL, "pkv_prefill_chunk: max_query_len %d needs %lld q-tiles x %d "
+                    "key splits", p.max_query_len, (long long)nqt, ks);
+    if (ks > 1 && (p.out_dtype != PKV_F32 || !p.lse || p.split_rows <= 0))
+        return fail(PKV_EINVAL, "pkv_prefill_chunk: key splits need fp32 states and lse");
     PArgs a;
     a.q = static_cast<const uint16_t *>(p.q);
     a.qsl = p.query_start;
@@ -553,9 +581,11 @@ int launch_prefill(const PrefillLaunch &p)
     a.causal = p.causal;
     a.q_shared = p.q_shared;
     a.lse = p.lse;
+    a.ks = ks;
+    a.split_rows = ks > 1 ? p.split_rows : 0;
     hipStream_t st = reinterpret_cast<hipStream_t>(p.stream);
-    hipLaunchKernelGGL(fn, dim3(p.num_kv_heads, (unsigned)nqt, p.num_seqs), dim3(kThreads), 0, st,
-                       a);
+    hipLaunchKernelGGL(fn, dim3(p.num_kv_heads, (unsigned)(nqt * ks), p.num_seqs), dim3(kThreads),
+                       0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(PKV_EHIP, "pkv_prefill_chunk: launch failed: %s", hipGetErrorString(e));

@@ -100,11 +100,22 @@ def prefill_state(batch: synth.PrefillBatch, pool_seed=None, poison=None):
     return cache, q, qs, tables, lens, max_len
 
 
+def prefill_workspace(S, Hq, max_query_len, desc, device="cuda"):
+    """The workspace pkv_prefill_chunk asks for (key-split states), or None."""
+    n = pkv.prefill_workspace_bytes(S, Hq, max_query_len, desc)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def run_prefill(cache: PagedCache, q, qs, tables, lens, max_len, scale, max_query_len,
-                out_dtype=torch.float32):
+                out_dtype=torch.float32, split=True):
+    """pkv_prefill_chunk; split=False passes no workspace (one pass per
+    workgroup over all its keys), split=True the workspace it asks for (the
+    library then splits the keys where the grid is short)."""
     out = torch.empty(tuple(q.shape), dtype=out_dtype, device=q.device)
+    ws = prefill_workspace(int(qs.numel()) - 1, int(q.shape[1]), max_query_len, cache.desc,
+                           q.device) if split else None
     pkv.prefill_chunk(q, qs, cache.k_cache, cache.v_cache, tables, lens, scale, out, cache.desc,
-                      max_query_len, max_len)
+                      max_query_len, max_len, workspace=ws)
     torch.cuda.synchronize()
     return out
 

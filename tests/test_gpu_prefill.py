@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import paged_kv_cache_indirected_amd as pkv
 import synth
 from harness import (TOL, decode_state, max_err, prefill_state, run_decode, run_prefill,
                      sample_rows, say)
@@ -119,6 +120,38 @@ def test_bf16_output():
     o = out.float().cpu().numpy().astype(np.float64)
     half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8)
     assert np.all(np.abs(o - ref) <= 2e-3 + half_ulp)
+
+
+@pytest.mark.parametrize("case", [
+    # (prior, chunk, Hq, Hkv, D, bs): few workgroups over long contexts, so
+    # the library splits the keys; the short sequence beside the long one has
+    # fewer key tiles than splits (empty splits).
+    ([3000, 0], [64, 16], 16, 2, 128, 16),
+    ([4000], [200], 64, 8, 128, 16),
+    ([2500, 1200, 7], [33, 128, 5], 8, 8, 64, 32),
+])
+def test_key_splits_match_single_pass_and_oracle(case):
+    prior, chunk, Hq, Hkv, D, bs = case
+    b = synth.custom_prefill(316 + len(prior), prior=prior, chunk=chunk, Hq=Hq, Hkv=Hkv, D=D,
+                             block_size=bs)
+    C = int(b.chunk.max())
+    ws = pkv.prefill_workspace_bytes(len(chunk), Hq, C, pkv.CacheDesc(
+        b.pool_blocks, Hkv, bs, D, pkv.BF16))
+    assert ws > 0, "expected a key-split workspace for this shape"
+    st = prefill_state(b)
+    o_split = run_prefill(*st, b.shape.scale, C, split=True)
+    o_one = run_prefill(*st, b.shape.scale, C, split=False)
+    say(f"[prefill] key splits prior={prior} chunk={chunk}: split vs single "
+        f"{(o_split - o_one).abs().max().item():.3e}")
+    # The merge is an exact rearrangement of the softmax sums: the two differ
+    # by fp32 rounding only.
+    assert torch.allclose(o_split, o_one, rtol=0, atol=1e-5)
+    ref = oracle.prefill(b.q, b.query_start, b.k, b.v, b.lens, b.shape.scale)
+    err = float(np.max(np.abs(o_split.cpu().numpy().astype(np.float64) - ref)))
+    assert np.isfinite(err) and err <= TOL["bf16"], err
+    o_bf = run_prefill(*st, b.shape.scale, C, out_dtype=torch.bfloat16, split=True)
+    half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8)
+    assert np.all(np.abs(o_bf.float().cpu().numpy().astype(np.float64) - ref) <= 2e-3 + half_ulp)
 
 
 def test_repeat_is_bitwise_deterministic():
