@@ -194,3 +194,20 @@ def test_decode_cascade_rejects():
     assert call(ws=None) == pkv.EINVAL
     assert call(B=0) == pkv.OK
     assert L.pkv_decode_cascade_workspace_bytes(2, 64, 32, 100, ctypes.byref(_desc())) > 0
+
+
+def test_prefill_workspace_sizes_key_split_states():
+    # A short grid (1 sequence x 4 q-tiles x 8 KV heads = 32 workgroups) asks
+    # for split states: k fp32 outputs and log2-sum-exps of S * max_query_len
+    # * Hq rows, each array 256-byte aligned; a grid of many workgroups, an
+    # fp32 cache or a head_dim without a kernel asks for none.
+    d = _desc()
+    rows = 1 * 64 * 64
+    n = L.pkv_prefill_workspace_bytes(1, 64, 64, ctypes.byref(d))
+    assert n > 0
+    per_split = (rows * d.head_dim * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert n % per_split == 0 and 2 <= n // per_split <= 16
+    assert L.pkv_prefill_workspace_bytes(64, 64, 4096, ctypes.byref(d)) == 0
+    assert L.pkv_prefill_workspace_bytes(1, 64, 64, ctypes.byref(_desc(dtype=pkv.F32))) == 0
+    assert L.pkv_prefill_workspace_bytes(1, 64, 64, ctypes.byref(_desc(head_dim=96))) == 0
+    assert L.pkv_prefill_workspace_bytes(0, 64, 64, ctypes.byref(d)) == 0
