@@ -66,6 +66,7 @@ constexpr int kThreads = NW * 64;
 constexpr float kLazyMax = 8.0f;      // running-max slack, log2 units
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data format, no swizzle
 constexpr int kIdChunk = 2 * kThreads; // block-table entries staged in LDS at a time
+constexpr int kDefer = 64;            // fused-append rows a workgroup writes at its end
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -403,6 +404,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     __shared__ int32_t lds_pref[kDecodeMaxSeqs + 1];
     __shared__ __attribute__((aligned(16))) uint4 lds_q[G * LPT];
     __shared__ __attribute__((aligned(16))) uint4 lds_new[2][LPT];   // fused append: K, V row
+    __shared__ int32_t lds_defer[kDefer];                            // ... sequences written last
     __shared__ int32_t lds_ids[kIdChunk];
     __shared__ int32_t lds_wsum[NW];
     __shared__ float lds_o[NW][G * OSTR];
@@ -484,6 +486,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     const uint32_t voff = DT == PKV_F32 ? (uint32_t)((g4 * D + n) * 16)
                                         : (uint32_t)((g4 * D + 2 * n) * 8);
 
+    int ndefer = 0;                    // deferred fused-append rows (uniform)
     int64_t x = start;
     while (x < end) {
         while (lds_pref[b + 1] <= x)
@@ -499,9 +502,13 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         // piece's first block ids and, for the fused append, the step's new
         // K/V rows of this KV head and their slot: all loads are issued
         // before any is waited for.  The workgroup holding the sequence's
-        // last block writes the new rows to their slot and keeps them in LDS
-        // so that the attention reads position L-1 from there rather than
-        // from the cache written in the same launch.
+        // last block keeps the new rows in LDS, so that the attention reads
+        // position L-1 from there rather than from the cache, and writes
+        // them to their slot after its last piece: no other workgroup of the
+        // launch reads that block, and stores issued mid-stream would hold
+        // up the tile loads (one in-order counter covers loads and stores;
+        // a lone row's stores are partial cache-line writes).  Beyond
+        // kDefer rows a workgroup writes them at once.
         const int n0 = j1 - j0 < kIdChunk ? j1 - j0 : kIdChunk;
         const bool last_piece = a.k_new && j1 == nblk;
         int32_t nslot = -1;
@@ -529,10 +536,16 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
                 lds_ids[tid + kThreads] = id1;
             if ((unsigned)nslot < (unsigned)(a.num_blocks * BS) && tid < 2 * LPT) {
                 lds_new[tid / LPT][tid % LPT] = nv;
-                store_new_chunk(a, nslot, g, tid / LPT, tid % LPT, nv);
+                if (ndefer >= kDefer)
+                    store_new_chunk(a, nslot, g, tid / LPT, tid % LPT, nv);
             }
         }
         const bool fresh = (unsigned)nslot < (unsigned)(a.num_blocks * BS);
+        if (fresh && ndefer < kDefer) {
+            if (tid == 0)
+                lds_defer[ndefer] = b;
+            ++ndefer;
+        }
         lds_barrier();
 
         // This lane's B operand of S = K Q^T: chunk 4 kk + g4 of query head
@@ -730,6 +743,18 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         lds_barrier();
         x = sb + j1;
         ++b;
+    }
+
+    // The deferred fused-append rows: 2 * LPT chunk stores per sequence
+    // (its K and V row of this KV head), the rows reloaded from k_new/v_new.
+    // lds_defer was written before the last piece's barriers.
+    for (int i = tid; i < ndefer * 2 * LPT; i += kThreads) {
+        const int k = i / (2 * LPT), u = i % (2 * LPT);
+        const int bd = lds_defer[k];
+        const int nslot = a.slots[bd];
+        const uint4 row = static_cast<const uint4 *>(u < LPT ? a.k_new : a.v_new)
+            [((int64_t)bd * a.Hkv + g) * LPT + u % LPT];
+        store_new_chunk(a, nslot, g, u / LPT, u % LPT, row);
     }
 }
 
