@@ -268,6 +268,62 @@ def bench_cfg3(timer, steps, splits):
             "pct_of_hbm_peak": round(100 * kvb / t / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def bench_decode_sweep(timer):
+    """Decode at batch sizes 1 .. 128, every sequence at context 4096
+    (64q/8kv, d128, bf16, 16-token blocks): the automatic split (about one
+    workgroup per CU, sequences cut across workgroups and merged) against
+    one workgroup per (sequence, KV head) (num_splits = B: with equal
+    lengths every range is exactly one sequence, nothing is merged).  Each
+    point rotates enough shuffled copies that they exceed the 256 MB
+    Infinity Cache.  The rows of one 4096-token sequence are reused for every
+    sequence (the values do not change the work)."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    import synth
+    L, Bmax = 4096, 128
+    base = synth.cfg2(B=1)
+    sh = base.shape
+    g = synth.rng(2, synth.S_K, 9)
+    rk = synth.normal(g, (L, sh.Hkv, sh.D), sh.dtype)
+    rv = synth.normal(synth.rng(2, synth.S_V, 9), (L, sh.Hkv, sh.D), sh.dtype)
+    res = {}
+    for B in (1, 2, 4, 8, 16, 32, 64, 128):
+        lens = np.full(B, L, dtype=np.int64)
+        b = synth.DecodeBatch(2, "sweep", sh, lens, synth.normal(synth.rng(2, synth.S_Q, 9, B),
+                              (B, sh.Hq, sh.D), sh.dtype), np.tile(rk, (B, 1, 1)),
+                              np.tile(rv, (B, 1, 1)), pool_blocks=B * (L // sh.block_size) + 8,
+                              pool_seed=base.pool_seed)
+        kv = float(B * L) * kv_row_bytes(sh)
+        R = int(min(64, max(1, np.ceil(1.1e9 / kv))))
+        states = [paged_state(b, b.pool_seed + 7919 * r) for r in range(R)]
+        for st in states:
+            c = st["cache"]
+            pkv.append(st["k_new"], st["v_new"], st["slots"], c.k_cache, c.v_cache, c.desc)
+        out = torch.empty((B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+        desc = states[0]["cache"].desc
+        entry = {"copies": R}
+        for label, W in (("auto_split", 0), ("one_wg_per_seq", B)):
+            ws = workspace(B, sh.Hq, L, desc, W)
+            it = [0]
+
+            def call():
+                st = states[it[0] % R]
+                it[0] += 1
+                c = st["cache"]
+                pkv.decode(st["q"], c.k_cache, c.v_cache, st["tables"], st["lens"], sh.scale, out,
+                           desc, L, workspace=ws, num_splits=W)
+            t = float(np.median(timer.per_call(call, max(2 * R, 40), warmup=R)))
+            entry[label] = {"ms": round(1e3 * t, 4), "kv_GBps": round(kv / t / 1e9, 1),
+                            "pct_of_hbm_peak": round(100 * kv / t / 1e9 / HBM_PEAK_GBS, 2)}
+        entry["split_speedup"] = round(entry["one_wg_per_seq"]["ms"] / entry["auto_split"]["ms"], 3)
+        res[f"B{B}"] = entry
+        del states
+        torch.cuda.empty_cache()
+    res["workload"] = ("decode at B = 1..128, every context 4096, 64q/8kv, d128, bf16, block 16: "
+                       "automatic split vs one workgroup per (sequence, KV head)")
+    return res
+
+
 def bench_cfg4(timer, splits):
     """Prefix-sharing decode: 128 sequences share one 2048-token prefix's
     physical blocks; logical bytes count the prefix once per sequence."""
@@ -750,7 +806,8 @@ def main():
                     help="skip the other workloads and the probes")
     ap.add_argument("--only", choices=["continuous_batching", "prefix_sharing",
                                        "chunked_prefill_mixed", "append", "block_copy",
-                                       "prefix_cache_ttft", "step_scheduler"],
+                                       "prefix_cache_ttft", "step_scheduler",
+                                       "decode_batch_sweep"],
                     help="run one secondary workload alone (for profiling) and print its JSON")
     ap.add_argument("--probe-copy", action="store_true",
                     help="run only the copy probe (for hardware-counter scaling)")
@@ -785,7 +842,8 @@ def main():
                "append": lambda: bench_append(timer),
                "block_copy": lambda: bench_block_copy(timer),
                "prefix_cache_ttft": lambda: bench_prefix_ttft(timer),
-               "step_scheduler": lambda: bench_sched()}
+               "step_scheduler": lambda: bench_sched(),
+               "decode_batch_sweep": lambda: bench_decode_sweep(timer)}
         print(json.dumps({args.only: fns[args.only]()}), flush=True)
         return
     batch = synth.cfg2()
@@ -913,6 +971,9 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] chunked prefill + decode")
         wl["chunked_prefill_mixed"] = bench_cfg5(timer, args.splits)
+        torch.cuda.empty_cache()
+        log("[bench] decode batch-size sweep")
+        wl["decode_batch_sweep"] = bench_decode_sweep(timer)
         torch.cuda.empty_cache()
         log("[bench] append")
         wl["append"] = bench_append(timer)

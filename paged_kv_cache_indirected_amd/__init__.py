@@ -359,7 +359,9 @@ def prefill_chunk(q, query_start_loc, k_cache, v_cache, block_tables, context_le
                   out, desc: CacheDesc, max_query_len: int, max_context_len: int, workspace=None,
                   stream=None) -> None:
     """pkv_prefill_chunk: causal attention of each sequence's chunk rows over
-    its paged context (the chunk already appended)."""
+    its paged context (the chunk already appended).  ``workspace`` (a uint8
+    GPU tensor of ``prefill_workspace_bytes(...)`` bytes, or None) lets the
+    library split the keys of a grid smaller than the device."""
     torch = _torch()
     S = int(query_start_loc.numel()) - 1
     _need(q.dim() == 3 and q.shape[2] == desc.head_dim and _dtype_code(q) == desc.dtype,
