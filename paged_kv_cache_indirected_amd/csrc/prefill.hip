@@ -15,10 +15,9 @@
 //   * 4 waves x 32 rows (NCT = 2 column tiles of 16; 48 rows per wave need
 //     more than half the register file, and one wave per SIMD ran 1.6x
 //     slower).  Keys are processed in tiles of 64.  The workgroup stages
-//     each tile of K ([64][D], row-major) and V (transposed, [D][64],
-//     keys in the MFMA k order) into LDS from the paged cache with coalesced
-//     16-byte loads (1 KiB runs of a block's tile; the cache's V tiles
-//     already hold 4 consecutive keys of a dim together), double buffered:
+//     each tile of K ([64][D], row-major) and V (in the cache's order: 4
+//     consecutive keys of a dim together) into LDS from the paged cache with
+//     coalesced 16-byte loads (1 KiB runs of a block's tile), double buffered:
 //     the next tile's global loads are in flight while the current tile is
 //     computed.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's
@@ -64,9 +63,9 @@ constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data forma
 template <int D>
 struct PShape {
     static constexpr int KSTR = D + 8;               // LDS row stride of K (elements)
-    static constexpr int VSTR = KT + 8;              // LDS row stride of V^T (elements)
+    static constexpr int VGS = 4 * D + 64;           // LDS stride of a 4-key V group (elements)
     static constexpr int KBUF = KT * KSTR;
-    static constexpr int VBUF = D * VSTR;
+    static constexpr int VBUF = (KT / 4) * VGS;
     static constexpr int NDS = D / 32;               // k-steps of S^T over head_dim
     static constexpr int NDT = D / 16;               // 16-row tiles of O^T
     static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -93,22 +92,6 @@ struct PArgs {
     int64_t split_rows;               // rows of one split's state (out / lse stride)
 };
 
-// LDS column of key kk (0..63) in the transposed V tile: the 8 keys a lane
-// feeds to one PV MFMA, {32s + 4q + i} and {32s + 16 + 4q + i} for i < 4,
-// sit next to each other.
-// Element offset of key position pos in row d of the transposed V tile:
-// 16-byte units are XOR-swizzled by the row's eighth, so the 16 rows that one
-// store instruction writes (d = 8 cc + e) fall on different LDS banks while a
-// lane's 8-key MFMA operand stays one aligned 16-byte read.
-__device__ __forceinline__ int vcol(int d, int pos)
-{
-    return (((pos >> 3) ^ ((d >> 3) & 7)) << 3) | (pos & 7);
-}
-
-__device__ __forceinline__ int vpos(int kk)
-{
-    return (kk & 32) | ((kk >> 2) & 3) << 3 | ((kk >> 4) & 1) << 2 | (kk & 3);
-}
 
 __device__ __forceinline__ uint16_t bf16_rne(float f)
 {
@@ -144,7 +127,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
     using Sh = PShape<D>;
     constexpr int TQ = ROWS / G;                     // chunk tokens per workgroup
     constexpr int NDS = Sh::NDS, NDT = Sh::NDT, CPR = Sh::CPR, VK = Sh::VK;
-    constexpr int KSTR = Sh::KSTR, VSTR = Sh::VSTR;
+    constexpr int KSTR = Sh::KSTR, VGS = Sh::VGS;
     constexpr int IDS = kIdChunk;                    // block ids staged per chunk
     constexpr int CT = IDS * BS / KT;                // key tiles per id chunk
 
@@ -297,10 +280,12 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
             }
         }
     };
-    // Registers -> LDS buffer: K rows as they are, V transposed with its
-    // keys placed in MFMA k order.  16-byte unit q of the wave's K part is
-    // chunk q / BS of token q % BS; unit q of its V part holds tokens
-    // 4 (2q / D) .. + 3 of dims 2 (q % (D / 2)) and the next.
+    // Registers -> LDS buffer: K rows as they are; V in the cache's own
+    // order, 4-key groups of [D][4] (group gi of the tile at gi * VGS, the
+    // 128-byte pad putting consecutive groups on opposite halves of the
+    // banks), so every store is a contiguous 16-byte run.  16-byte unit q of
+    // the wave's K part is chunk q / BS of token q % BS; unit q of its V part
+    // holds tokens 4 (2q / D) .. + 3 of dims 2 (q % (D / 2)) and the next.
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < Sh::KLD; ++i) {
@@ -311,12 +296,9 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
 #pragma unroll
         for (int e = 0; e < VK; ++e) {
             const int q = (wp * VK + e) * 64 + lane;
-            const int k0 = wblk + 4 * ((2 * q) / D);
+            const int gi = wblk / 4 + (2 * q) / D;
             const int d0 = 2 * (q % (D / 2));
-            *reinterpret_cast<uint2 *>(&lds_v[buf][d0 * VSTR + vcol(d0, vpos(k0))]) =
-                make_uint2(vst[e].x, vst[e].y);
-            *reinterpret_cast<uint2 *>(&lds_v[buf][(d0 + 1) * VSTR + vcol(d0 + 1, vpos(k0))]) =
-                make_uint2(vst[e].z, vst[e].w);
+            *reinterpret_cast<uint4 *>(&lds_v[buf][gi * VGS + d0 * 4]) = vst[e];
         }
     };
 
@@ -453,9 +435,14 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
         // the one just before it to finish accumulating.
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+            // A operand of dims dt*16 + n: k slots 8 quad + 4 half + i hold key
+            // 32 s2 + 16 half + 4 quad + i (the order of P^T's B operand), i.e.
+            // the 4 keys of dim d in groups 8 s2 + quad and 8 s2 + 4 + quad.
             auto vload = [&](int dt) {
-                return *reinterpret_cast<const bf16x8 *>(
-                    &lds_v[buf][(dt * 16 + n) * VSTR + vcol(dt * 16 + n, 32 * s2 + 8 * quad)]);
+                const uint16_t *v0 = &lds_v[buf][(8 * s2 + quad) * VGS + (dt * 16 + n) * 4];
+                const uint2 lo = *reinterpret_cast<const uint2 *>(v0);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(v0 + 4 * VGS);
+                return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
             };
             bf16x8 vprev = vload(0);
 #pragma unroll
