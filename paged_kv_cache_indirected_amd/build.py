@@ -62,7 +62,9 @@ def build(verbose: bool = False) -> str:
                 print(r.stdout, r.stderr, file=sys.stderr)
     tmp = LIB + ".tmp"
     objs = [os.path.join(OBJ, s + ".o") for s in HOST_SRC + HIP_SRC]
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+    # -z defs: a symbol left undefined (e.g. a kernel whose host stub was not
+    # emitted) fails the build instead of the library's first load.
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp"
     _run([hipcc, *HIP_FLAGS, "-shared", os.path.join(CSRC, "probe.hip"), "-o", tmp])
