@@ -314,16 +314,14 @@ int32_t cascade_splits(int32_t B, int32_t hq, int32_t nb, const pkv_cache_desc *
 }
 
 struct CascadeWs {
-    size_t qs, lens, o, lse, dws, total;
+    size_t o, lse, dws, total;
 };
 
 CascadeWs cascade_layout(int32_t B, int32_t hq, int32_t D, int32_t ks, int32_t W)
 {
     const size_t rows = (size_t)B * hq, states = (size_t)ks + 1;
     CascadeWs l;
-    l.qs = 0;
-    l.lens = align256(((size_t)ks + 1) * sizeof(int32_t));
-    l.o = l.lens + align256(((size_t)ks + 1) * sizeof(int32_t));
+    l.o = 0;
     l.lse = l.o + align256(states * rows * D * sizeof(float));
     l.dws = l.lse + align256(states * rows * sizeof(float));
     l.total = l.dws + ws_layout(B, hq, W, D).total;
@@ -430,19 +428,19 @@ extern "C" int pkv_decode_cascade(const void *q, const void *k_cache, const void
     if (ks > 0) {
         // The shared prefix once for all sequences: ks pseudo-sequences, one
         // per range of prefix blocks, each holding every sequence's queries
-        // (read from the same rows) and attending its whole range.
+        // (read from the same rows) and attending its whole range; the
+        // kernel derives each one's query rows and key count itself.
         const int32_t nbk = (nb + ks - 1) / ks;
-        int32_t *qs = reinterpret_cast<int32_t *>(ws + lay.qs);
-        int32_t *lens = reinterpret_cast<int32_t *>(ws + lay.lens);
-        if ((rc = pkv::launch_cascade_setup(qs, lens, ks, num_seqs, nbk, nb, c->block_size,
-                                            stream)))
-            return rc;
-        pkv::PrefillLaunch p{q, qs, ks, num_seqs, k_cache, v_cache, prefix_blocks, nbk, lens,
-                             nbk * c->block_size, num_q_heads, c->num_kv_heads, c->num_blocks,
-                             c->block_size, c->head_dim, scale, o_all, PKV_F32, stream};
+        pkv::PrefillLaunch p{q, nullptr, ks, num_seqs, k_cache, v_cache, prefix_blocks, nbk,
+                             nullptr, nbk * c->block_size, num_q_heads, c->num_kv_heads,
+                             c->num_blocks, c->block_size, c->head_dim, scale, o_all, PKV_F32,
+                             stream};
         p.causal = 0;
         p.q_shared = 1;
         p.lse = lse_all;
+        p.syn_rows = num_seqs;
+        p.syn_nbk = nbk;
+        p.syn_nb = nb;
         if ((rc = pkv::launch_prefill(p)))
             return rc;
     }

@@ -762,29 +762,33 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
 // between workgroups: M = max_p m_p, L = sum_p l_p 2^(m_p - M),
 // out = sum_p o_p 2^(m_p - M) / L, taken in workgroup order over the
 // workgroups whose ranges hold blocks of the sequence.  One workgroup per
-// (sequence, query head), one thread per output element; the pieces of a
-// sequence are consecutive in the workspace and are loaded in batches whose
-// loads are in flight together.  Empty sequences get zeros here; sequences
-// held whole by one workgroup were written by it.
+// (sequence, KV head): a piece's G query heads x D dims are contiguous in
+// the workspace, so each thread folds 4 consecutive values (16-byte loads)
+// and the grid stays small (the kernel's time follows its workgroup count,
+// not its bytes).  Pieces are read 8 at a time, all loads of a batch in
+// flight together.  Empty sequences get zeros here; sequences held whole by
+// one workgroup were written by it.
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void k_merge(Args a)
+__global__ __launch_bounds__(kMergeThreads) void k_merge(Args a)
 {
-    const int b = blockIdx.x, hq = blockIdx.y, d = threadIdx.x;
+    const int b = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
     const int G = a.Hq / a.Hkv;
-    const int g = hq / G, h = hq - g * G;
     const int64_t Ct = (int64_t)a.ws_pref[a.B] + (int64_t)a.piece_cost * a.B;
     const int sb = a.ws_pref[b], se = a.ws_pref[b + 1];
-    const int64_t oidx = ((int64_t)b * a.Hq + hq) * D + d;
+    const int64_t obase = ((int64_t)b * a.Hq + (int64_t)g * G) * D;   // head g*G, dim 0
     if (se == sb) {
-        store_out(a.out, a.out_dtype, oidx, 0.0f);
-        if (a.lse && d == 0)
-            a.lse[(int64_t)b * a.Hq + hq] = -INFINITY;
+        for (int i = tid; i < G * D; i += kMergeThreads)
+            store_out(a.out, a.out_dtype, obase + i, 0.0f);
+        if (a.lse && tid < G)
+            a.lse[(int64_t)b * a.Hq + g * G + tid] = -INFINITY;
         // Fused append of a sequence with no blocks: no split workgroup
         // visits it, so its new row is written here.
-        if (a.k_new && h == 0 && d < 2 * a.row_chunks) {
+        if (a.k_new && tid < 2 * a.row_chunks) {
             const int nslot = a.slots[b];
             if ((unsigned)nslot < (unsigned)(a.num_blocks * a.block_size)) {
-                const int kv = d / a.row_chunks, i = d % a.row_chunks;
+                const int kv = tid / a.row_chunks, i = tid % a.row_chunks;
                 const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
                     [((int64_t)b * a.Hkv + g) * a.row_chunks + i];
                 store_new_chunk(a, nslot, g, kv, i, row);
@@ -797,70 +801,92 @@ __global__ __launch_bounds__(D) void k_merge(Args a)
     if (wf == wl)
         return;
     const bool sparse = Ct < a.W;   // only then can a range be empty
-    // Piece (w + b) of KV head g, query head h within the group.  Pieces
-    // are read 8 at a time, all loads of a batch in flight together, and
-    // folded into a running (M, L, O) in workgroup order.
-    const int64_t p0 = ((int64_t)g * (a.W + a.B) + b) * G + h;
-    float M = -INFINITY, Ls = 0.0f, O = 0.0f;
-    for (int w0 = wf; w0 <= wl; w0 += 8) {
-        float mp[8], lp[8], op[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int w = w0 + k;
-            const bool use = w <= wl && !(sparse && empty_range(w, Ct, a.W));
-            const int64_t pr = p0 + (int64_t)w * G;
-            mp[k] = use ? a.ws_ml[pr * 2] : -INFINITY;
-            lp[k] = use ? a.ws_ml[pr * 2 + 1] : 0.0f;
-            op[k] = use ? a.ws_o[pr * D + d] : 0.0f;
-        }
-        float Mn = M;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            Mn = fmaxf(Mn, mp[k]);
-        if (Mn != -INFINITY) {
-            const float f0 = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-            Ls *= f0;
-            O *= f0;
+    // Piece (w + b) of KV head g holds rows (head h, dim d) at
+    // ((g * (W + B) + w + b) * G + h) * D + d.
+    const int64_t p0 = ((int64_t)g * (a.W + a.B) + b) * G;
+    for (int i4 = tid; i4 < G * D / 4; i4 += kMergeThreads) {
+        const int h = (4 * i4) / D, d0 = (4 * i4) % D;
+        float M = -INFINITY, Ls = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int w0 = wf; w0 <= wl; w0 += 8) {
+            float mp[8], lp[8];
+            f32x4 op[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float f = (mp[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp[k] - Mn);
-                Ls = __builtin_fmaf(lp[k], f, Ls);
-                O = __builtin_fmaf(op[k], f, O);
+                const int w = w0 + k;
+                const bool use = w <= wl && !(sparse && empty_range(w, Ct, a.W));
+                const int64_t pr = p0 + (int64_t)w * G + h;
+                mp[k] = use ? a.ws_ml[pr * 2] : -INFINITY;
+                lp[k] = use ? a.ws_ml[pr * 2 + 1] : 0.0f;
+                op[k] = use ? *reinterpret_cast<const f32x4 *>(a.ws_o + pr * D + d0)
+                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
+            float Mn = M;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                Mn = fmaxf(Mn, mp[k]);
+            if (Mn != -INFINITY) {
+                const float f0 = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+                Ls *= f0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    O[e] *= f0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float f = (mp[k] == -INFINITY) ? 0.0f
+                                                         : __builtin_amdgcn_exp2f(mp[k] - Mn);
+                    Ls = __builtin_fmaf(lp[k], f, Ls);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        O[e] = __builtin_fmaf(op[k][e], f, O[e]);
+                }
+            }
+            M = Mn;
         }
-        M = Mn;
+        const int64_t oidx = obase + (int64_t)h * D + d0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            store_out(a.out, a.out_dtype, oidx + e, Ls > 0.0f ? O[e] / Ls : 0.0f);
+        if (a.lse && d0 == 0)
+            a.lse[(int64_t)b * a.Hq + g * G + h] = Ls > 0.0f ? M + __log2f(Ls) : -INFINITY;
     }
-    store_out(a.out, a.out_dtype, oidx, Ls > 0.0f ? O / Ls : 0.0f);
-    if (a.lse && d == 0)
-        a.lse[(int64_t)b * a.Hq + hq] = Ls > 0.0f ? M + __log2f(Ls) : -INFINITY;
 }
 
 // Log-sum-exp merge of K attention states of the same rows (each state a
-// normalised output and its log2-sum-exp), in state order.  One workgroup
-// per row, one thread per output element.
+// normalised output and its log2-sum-exp), in state order.  Each thread
+// folds 4 consecutive dims of one row (16-byte loads); a 256-thread
+// workgroup takes 1024 / D rows.
 template <int D>
-__global__ __launch_bounds__(D) void k_merge_states(const float *__restrict__ o,
-                                                    const float *__restrict__ lse, int32_t K,
-                                                    int64_t rows, void *out, int32_t out_dtype,
-                                                    const int32_t *row_tokens, int32_t heads)
+__global__ __launch_bounds__(kMergeThreads) void k_merge_states(const float *__restrict__ o,
+                                                                const float *__restrict__ lse,
+                                                                int32_t K, int64_t rows,
+                                                                void *out, int32_t out_dtype,
+                                                                const int32_t *row_tokens,
+                                                                int32_t heads)
 {
-    const int64_t r = blockIdx.x;
-    const int d = threadIdx.x;
-    if (row_tokens && r >= (int64_t)row_tokens[0] * heads)
+    constexpr int TPR = D / 4;                       // threads per row
+    constexpr int RPW = kMergeThreads / TPR;         // rows per workgroup
+    const int64_t r = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+    const int d0 = (threadIdx.x % TPR) * 4;
+    if (r >= rows || (row_tokens && r >= (int64_t)row_tokens[0] * heads))
         return;
     float M = -INFINITY;
     for (int k = 0; k < K; ++k)
         M = fmaxf(M, lse[k * rows + r]);
-    float W = 0.0f, O = 0.0f;
+    float W = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (M != -INFINITY) {
         for (int k = 0; k < K; ++k) {
             const float lk = lse[k * rows + r];
             const float f = (lk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lk - M);
             W += f;
-            O = __builtin_fmaf(o[(k * rows + r) * D + d], f, O);
+            const f32x4 ok = *reinterpret_cast<const f32x4 *>(o + (k * rows + r) * D + d0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                O[e] = __builtin_fmaf(ok[e], f, O[e]);
         }
     }
-    store_out(out, out_dtype, r * D + d, W > 0.0f ? O / W : 0.0f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        store_out(out, out_dtype, r * D + d0 + e, W > 0.0f ? O[e] / W : 0.0f);
 }
 
 using KernelFn = void (*)(Args);
@@ -973,38 +999,11 @@ int launch_decode(const DecodeLaunch &d)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return fail(PKV_EHIP, "pkv_decode: launch failed: %s", hipGetErrorString(e));
-        hipLaunchKernelGGL(merge, dim3(nb, d.num_q_heads), dim3(d.head_dim), 0, st, a);
+        hipLaunchKernelGGL(merge, dim3(nb, d.num_kv_heads), dim3(kMergeThreads), 0, st, a);
         e = hipGetLastError();
         if (e != hipSuccess)
             return fail(PKV_EHIP, "pkv_decode: merge launch failed: %s", hipGetErrorString(e));
     }
-    return PKV_OK;
-}
-
-namespace {
-
-// Query offsets and key counts of the shared-prefix pseudo-sequences of a
-// cascade decode: split k holds prefix blocks [k nbk, min((k+1) nbk, nb)).
-__global__ void k_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int32_t nbk,
-                                int32_t nb, int32_t bs)
-{
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k <= ks)
-        qs[k] = k * B;
-    if (k < ks)
-        lens[k] = min(nbk, nb - k * nbk) * bs;
-}
-
-}  // namespace
-
-int launch_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int32_t nbk,
-                         int32_t nb, int32_t bs, void *stream)
-{
-    hipLaunchKernelGGL(k_cascade_setup, dim3((ks + 64) / 64), dim3(64), 0,
-                       reinterpret_cast<hipStream_t>(stream), qs, lens, ks, B, nbk, nb, bs);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return fail(PKV_EHIP, "cascade setup launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
 
@@ -1018,11 +1017,13 @@ int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t row
         return fail(PKV_EINVAL, "merge of %lld rows", (long long)rows);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 64)
-        hipLaunchKernelGGL(k_merge_states<64>, dim3((unsigned)rows), dim3(64), 0, st, o, lse, k,
-                           rows, out, out_dtype, row_tokens, heads);
+        hipLaunchKernelGGL(k_merge_states<64>, dim3((unsigned)((rows + 15) / 16)),
+                           dim3(kMergeThreads), 0, st, o, lse, k, rows, out, out_dtype,
+                           row_tokens, heads);
     else
-        hipLaunchKernelGGL(k_merge_states<128>, dim3((unsigned)rows), dim3(128), 0, st, o, lse, k,
-                           rows, out, out_dtype, row_tokens, heads);
+        hipLaunchKernelGGL(k_merge_states<128>, dim3((unsigned)((rows + 7) / 8)),
+                           dim3(kMergeThreads), 0, st, o, lse, k, rows, out, out_dtype,
+                           row_tokens, heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(PKV_EHIP, "state merge launch failed: %s", hipGetErrorString(e));

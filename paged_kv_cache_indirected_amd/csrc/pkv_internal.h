@@ -59,9 +59,6 @@ int32_t decode_piece_cost(int32_t block_size, int32_t head_dim, int32_t elem_siz
 int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t rows,
                         int32_t head_dim, void *out, int32_t out_dtype, void *stream,
                         const int32_t *row_tokens = nullptr, int32_t heads = 0);
-// qs[k] = k B (k <= ks), lens[k] = min(nbk, nb - k nbk) bs (k < ks).
-int launch_cascade_setup(int32_t *qs, int32_t *lens, int32_t ks, int32_t B, int32_t nbk,
-                         int32_t nb, int32_t bs, void *stream);
 // Compute units of the current device (256 if it cannot be queried).
 int32_t device_cu_count();
 
@@ -121,6 +118,11 @@ struct PrefillLaunch {
     float *lse = nullptr;      // optional [rows][Hq] log2-sum-exp of the scaled scores
     int32_t key_splits = 1;    // > 1: split k writes its fp32 state at out + k * split_rows * D
     int64_t split_rows = 0;    //      and its log2-sum-exp at lse + k * split_rows
+    // syn_rows > 0: sequence s is range s of one block list (block_tables,
+    // stride syn_nbk, syn_nb blocks in all): syn_rows query rows from row
+    // s * syn_rows, min(syn_nbk, syn_nb - s * syn_nbk) blocks of keys;
+    // query_start and context_lens are not read.
+    int32_t syn_rows = 0, syn_nbk = 0, syn_nb = 0;
 };
 int launch_prefill(const PrefillLaunch &a);
 // Query rows (GQA-packed (token, head) pairs) one prefill workgroup holds.

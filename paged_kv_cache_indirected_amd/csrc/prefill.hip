@@ -90,7 +90,17 @@ struct PArgs {
     float scale_log2;
     int32_t ks;                       // key splits: split k writes state k (fp32 out + lse)
     int64_t split_rows;               // rows of one split's state (out / lse stride)
+    // syn_rows > 0: the sequences are the ranges of one block list (cascade
+    // prefix): sequence s has syn_rows query rows from row s * syn_rows and
+    // min(syn_nbk, syn_nb - s * syn_nbk) blocks of keys (qsl, lens unused).
+    int32_t syn_rows, syn_nbk, syn_nb;
 };
+
+template <int BS>
+__device__ __forceinline__ int seq_len(const PArgs &a, int s)
+{
+    return a.syn_rows > 0 ? min(a.syn_nbk, a.syn_nb - s * a.syn_nbk) * BS : a.lens[s];
+}
 
 
 __device__ __forceinline__ uint16_t bf16_rne(float f)
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
     int s = blockIdx.z;
     if (a.S <= 64) {
         const int i = lane < a.S ? lane : 0;
-        const int wi = a.lens[i];
+        const int wi = seq_len<BS>(a, i);
         int rank = 0;
         for (int j = 0; j < a.S; ++j) {
             const int wj = __builtin_amdgcn_readlane(wi, j);
@@ -158,9 +168,9 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
         s = hit ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit)) : blockIdx.z;
     }
 
-    const int q0 = a.qsl[s];
-    const int C = a.qsl[s + 1] - q0;
-    int L = a.lens[s];
+    const int q0 = a.syn_rows > 0 ? s * a.syn_rows : a.qsl[s];
+    const int C = a.syn_rows > 0 ? a.syn_rows : a.qsl[s + 1] - q0;
+    int L = seq_len<BS>(a, s);
     const int cap = a.stride * BS;
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int p0 = L - C;                            // keys before the chunk
@@ -570,6 +580,9 @@ int launch_prefill(const PrefillLaunch &p)
     a.lse = p.lse;
     a.ks = ks;
     a.split_rows = ks > 1 ? p.split_rows : 0;
+    a.syn_rows = p.syn_rows;
+    a.syn_nbk = p.syn_nbk;
+    a.syn_nb = p.syn_nb;
     hipStream_t st = reinterpret_cast<hipStream_t>(p.stream);
     hipLaunchKernelGGL(fn, dim3(p.num_kv_heads, (unsigned)(nqt * ks), p.num_seqs), dim3(kThreads),
                        0, st, a);
