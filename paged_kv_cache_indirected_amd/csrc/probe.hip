@@ -47,9 +47,10 @@ __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4 *__restric
 // tiles[i] = index of a (block, head) tile of tile_bytes in each of k and v.
 // Wave v of the grid reads tiles [v * per, (v + 1) * per) of the list, in
 // order, as the decode's workgroups read their ranges: 64 tile indices are
-// fetched in one load (lane i holds the i-th) and read back with readlane,
-// so no data load waits on an index load; two tiles (both tensors) are in
-// flight at a time, 1 KiB per wave load.
+// fetched in one load (lane i holds the i-th) and read back with readlane;
+// the next 64 are loaded while the current ones are read, so no data load
+// waits on an index load; two tiles (both tensors) are in flight at a time,
+// 1 KiB per wave load.
 __global__ __launch_bounds__(kThreads) void k_tile_read(const char *__restrict__ kc,
                                                         const char *__restrict__ vc,
                                                         const int64_t *__restrict__ tiles,
@@ -64,9 +65,11 @@ __global__ __launch_bounds__(kThreads) void k_tile_read(const char *__restrict__
     const int64_t t1 = t0 + per < ntiles ? t0 + per : ntiles;
     const int runs = tile_bytes / 1024;
     uint32_t acc = 0;
+    int64_t next = t0 + lane < t1 ? tiles[t0 + lane] : 0;
     for (int64_t base = t0; base < t1; base += 64) {
         const int nt = (int)(t1 - base < 64 ? t1 - base : 64);
-        const int64_t my = lane < nt ? tiles[base + lane] : 0;
+        const int64_t my = next;
+        next = base + 64 + lane < t1 ? tiles[base + 64 + lane] : 0;
         const uint32_t lo = (uint32_t)my, hi = (uint32_t)(my >> 32);
         for (int j = 0; j < nt; j += 2) {
             // A pair of tiles, or the last tile alone (the second tile's
