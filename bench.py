@@ -441,10 +441,26 @@ def bench_cfg5(timer, splits):
         ev1 = torch.cuda.Event()
         ev1.record(side)
         main.wait_event(ev1)
+    def step_two_streams_decode_first():
+        main = torch.cuda.current_stream()
+        ev0 = torch.cuda.Event()
+        ev0.record(main)
+        side.wait_event(ev0)
+        with torch.cuda.stream(side):
+            pkv.append(ds["k_new"], ds["v_new"], ds["slots"], dc.k_cache, dc.v_cache, dc.desc,
+                       stream=side)
+            pkv.decode(ds["q"], dc.k_cache, dc.v_cache, ds["tables"], ds["lens"], sh.scale, dout,
+                       dc.desc, ds["max_len"], workspace=ws, num_splits=splits, stream=side)
+        pkv.append(ck, cv, cslots, pc.k_cache, pc.v_cache, pc.desc)
+        prefill()
+        ev1 = torch.cuda.Event()
+        ev1.record(side)
+        main.wait_event(ev1)
     t_pre = float(np.median(timer.per_call(prefill, 10)))
     t_dec = float(np.median(timer.per_call(decode, 20)))
     t_step = float(np.median(timer.per_call(step, 10)))
     t_step2 = float(np.median(timer.per_call(step_two_streams, 10)))
+    t_step3 = float(np.median(timer.per_call(step_two_streams_decode_first, 10)))
     flops = sum(4.0 * sh.Hq * sh.D * (int(c) * int(p) + int(c) * (int(c) + 1) / 2)
                 for p, c in zip(pre.prior, pre.chunk))
     dbytes = float(dec.lens.sum()) * kv_row_bytes(sh)
@@ -464,6 +480,7 @@ def bench_cfg5(timer, splits):
             "step_two_streams_ms": round(1e3 * t_step2, 4),
             "step_two_streams_note": "prefill (with its append) on the launch stream, decode "
                                      "(with its append) on a second stream, joined by events",
+            "step_two_streams_decode_first_ms": round(1e3 * t_step3, 4),
             "short_chunk": bench_short_chunk(timer)}
 
 
