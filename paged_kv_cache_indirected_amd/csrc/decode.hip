@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     __shared__ int32_t lds_pref[kDecodeMaxSeqs + 1];
     __shared__ __attribute__((aligned(16))) uint4 lds_q[G * LPT];
     __shared__ __attribute__((aligned(16))) uint4 lds_new[2][LPT];   // fused append: K, V row
-    __shared__ int32_t lds_defer[kDefer];                            // ... sequences written last
+    __shared__ int32_t lds_defer[kDefer];     // fused append: sequences whose rows are written at the end
     __shared__ int32_t lds_ids[kIdChunk];
     __shared__ int32_t lds_wsum[NW];
     __shared__ float lds_o[NW][G * OSTR];
