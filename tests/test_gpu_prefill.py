@@ -149,6 +149,16 @@ def test_key_splits_match_single_pass_and_oracle(case):
     ref = oracle.prefill(b.q, b.query_start, b.k, b.v, b.lens, b.shape.scale)
     err = float(np.max(np.abs(o_split.cpu().numpy().astype(np.float64) - ref)))
     assert np.isfinite(err) and err <= TOL["bf16"], err
+    # A workspace shorter than asked for: the library splits less (or not
+    # at all) and the result is the same up to fp32 rounding.
+    cache, q, qs, tables, lens, mx = st
+    for frac in (2, 5):
+        short = torch.empty(ws // frac, dtype=torch.uint8, device="cuda")
+        o_short = torch.empty_like(o_one)
+        pkv.prefill_chunk(q, qs, cache.k_cache, cache.v_cache, tables, lens, b.shape.scale,
+                          o_short, cache.desc, C, mx, workspace=short)
+        torch.cuda.synchronize()
+        assert torch.allclose(o_short, o_one, rtol=0, atol=1e-5), frac
     o_bf = run_prefill(*st, b.shape.scale, C, out_dtype=torch.bfloat16, split=True)
     half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8)
     assert np.all(np.abs(o_bf.float().cpu().numpy().astype(np.float64) - ref) <= 2e-3 + half_ulp)
