@@ -255,13 +255,22 @@ def _step_state(batch, pool_seed=None):
             to_device_rows(batch.q, DT[sh.dtype], "cuda"), tables, lens, mx)
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg2", "ragged-bs32-f32"])
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "ragged-bs32-f32", "many-short"])
 def test_append_decode_equals_append_then_decode_bitwise(name):
     import paged_kv_cache_indirected_amd as pkv
+    splits = (0, 3)
     if name == "cfg1":
         b = synth.cfg1()
     elif name == "cfg2":
         b = synth.cfg2(B=8)
+    elif name == "many-short":
+        # 150 sequences of 1..40 tokens: with one workgroup per KV head it
+        # holds the last block of every sequence, more new rows than it keeps
+        # for the end of its range, so the rest are written at once.
+        lens = np.random.default_rng(17).integers(1, 41, size=150)
+        b = synth.custom_decode(17, lens.tolist(), Hq=16, Hkv=2, D=128, dtype="bf16",
+                                block_size=16)
+        splits = (0, 1, 3)
     else:
         b = synth.custom_decode(15, [1, 2, 31, 32, 33, 100], Hq=8, Hkv=2, D=128, dtype="f32",
                                 block_size=32)
@@ -269,7 +278,7 @@ def test_append_decode_equals_append_then_decode_bitwise(name):
     cache, slots, kn, vn, q, tab, lens, mx = _step_state(b)
     kc0, vc0 = cache.k_cache.clone(), cache.v_cache.clone()
     B, Hq, D = q.shape
-    for ns in (0, 3):
+    for ns in splits:
         ws = torch.zeros(pkv.decode_workspace_bytes(B, Hq, mx, cache.desc, ns), dtype=torch.uint8,
                          device="cuda")
         cache.k_cache.copy_(kc0)
