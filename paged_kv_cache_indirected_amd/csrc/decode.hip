@@ -869,19 +869,41 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_states(const float *__r
     const int d0 = (threadIdx.x % TPR) * 4;
     if (r >= rows || (row_tokens && r >= (int64_t)row_tokens[0] * heads))
         return;
+    // States are read 8 at a time, all loads of a batch in flight together,
+    // and folded in state order.
     float M = -INFINITY;
-    for (int k = 0; k < K; ++k)
-        M = fmaxf(M, lse[k * rows + r]);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        float lk[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            lk[j] = k0 + j < K ? lse[(int64_t)(k0 + j) * rows + r] : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            M = fmaxf(M, lk[j]);
+    }
     float W = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (M != -INFINITY) {
-        for (int k = 0; k < K; ++k) {
-            const float lk = lse[k * rows + r];
-            const float f = (lk == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lk - M);
-            W += f;
-            const f32x4 ok = *reinterpret_cast<const f32x4 *>(o + (k * rows + r) * D + d0);
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float lk[8];
+            f32x4 ok[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                O[e] = __builtin_fmaf(ok[e], f, O[e]);
+            for (int j = 0; j < 8; ++j) {
+                const bool use = k0 + j < K;
+                const int64_t row = (int64_t)(k0 + j) * rows + r;
+                lk[j] = use ? lse[row] : -INFINITY;
+                ok[j] = use ? *reinterpret_cast<const f32x4 *>(o + row * D + d0)
+                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (k0 + j >= K)
+                    break;
+                const float f = (lk[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lk[j] - M);
+                W += f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    O[e] = __builtin_fmaf(ok[j][e], f, O[e]);
+            }
         }
     }
 #pragma unroll
