@@ -215,15 +215,17 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (valid[ct]) {
-                v = *reinterpret_cast<const uint4 *>(a.q + qin[ct] + ds * 32 + quad * 8);
-                v.x ^= qsign;
-                v.y ^= qsign;
-                v.z ^= qsign;
-                v.w ^= qsign;
-            }
-            qf[ct][ds] = __builtin_bit_cast(bf16x8, v);
+            // Unconditional load (row 0 for a padding column, which the
+            // chunk always has), so all of the wave's q loads are in flight
+            // together; a load under the condition was waited for alone.
+            // (The mask is applied arithmetically: a select lets the
+            // compiler move the load back under the condition.)
+            const uint4 v = *reinterpret_cast<const uint4 *>(
+                a.q + (valid[ct] ? qin[ct] : 0) + ds * 32 + quad * 8);
+            const uint32_t mk = 0u - (uint32_t)valid[ct];
+            const uint4 x = make_uint4((v.x ^ qsign) & mk, (v.y ^ qsign) & mk,
+                                       (v.z ^ qsign) & mk, (v.w ^ qsign) & mk);
+            qf[ct][ds] = __builtin_bit_cast(bf16x8, x);
         }
 
     const int32_t *bt = a.tables + (int64_t)s * a.stride;
@@ -234,10 +236,20 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
     const int nblk = (kend + BS - 1) / BS;           // blocks the workgroup reads
 
     // Block ids of the key range staged through LDS, IDS at a time.
+    // All loads first (at a clamped index; nblk >= 1 whenever ids are
+    // staged), then the LDS stores, so the loads are in flight together.
     auto stage_ids = [&](int chunk) {
-        for (int i = tid; i < IDS; i += kThreads) {
-            const int jb = chunk * IDS + i;
-            lds_ids[i] = jb < nblk ? bt[jb] : -1;
+        constexpr int PER = IDS / kThreads;
+        int idv[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int jb = chunk * IDS + tid + k * kThreads;
+            idv[k] = bt[jb < nblk ? jb : nblk - 1];
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int jb = chunk * IDS + tid + k * kThreads;
+            lds_ids[tid + k * kThreads] = jb < nblk ? idv[k] : -1;
         }
     };
 
