@@ -205,15 +205,15 @@ __device__ __forceinline__ float rows_reduce(float v)
     return v;
 }
 
-// Context length of sequence b, clamped to what its table row addresses and
-// to the host's bound.
+// A context length clamped to what a table row addresses and to the host's
+// bound.
 template <int BS>
-__device__ __forceinline__ int clamp_len(const Args &a, int b)
+__device__ __forceinline__ int clamp_raw_len(const Args &a, int L)
 {
-    const int L = a.lens[b];
     const int cap = min(a.stride * BS, a.max_len);
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
+
 
 // Balanced ranges.  Flattened block x of sequence b costs x + pc * b:
 // besides its blocks, a workgroup pays a fixed time at every sequence
@@ -402,6 +402,11 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     constexpr int NSUB = Sh::NSUB, TILE = Sh::TILE, OSTR = Sh::OSTR;
 
     __shared__ int32_t lds_pref[kDecodeMaxSeqs + 1];
+    // Each sequence's clamped length and (fused append) slot, read with the
+    // lengths at the start: a piece's set-up then needs no global read but
+    // its q rows, block ids and new rows, all in flight together.
+    __shared__ int32_t lds_len[kDecodeMaxSeqs];
+    __shared__ int32_t lds_slot[kDecodeMaxSeqs];
     __shared__ __attribute__((aligned(16))) uint4 lds_q[G * LPT];
     __shared__ __attribute__((aligned(16))) uint4 lds_new[2][LPT];   // fused append: K, V row
     __shared__ int32_t lds_defer[kDefer];     // fused append: sequences whose rows are written at the end
@@ -421,7 +426,19 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     // writes the whole table itself, so it reads it back with no barrier
     // (the other waves write the same values).
     if (a.B <= 64) {
-        int v = lane < a.B ? (clamp_len<BS>(a, lane) + BS - 1) / BS : 0;
+        // Both loads unconditional (sequence 0 for idle lanes; slots read
+        // from the lengths when there is no fused append), so they are in
+        // flight together: a load under a condition is waited for alone.
+        const int32_t *sp = a.k_new ? a.slots : a.lens;
+        const int bi = lane < a.B ? lane : 0;
+        const int rl = a.lens[bi], sr = sp[bi];
+        const int Lb = lane < a.B ? clamp_raw_len<BS>(a, rl) : 0;
+        const int sl = a.k_new ? sr : -1;
+        if (lane < a.B) {
+            lds_len[lane] = Lb;
+            lds_slot[lane] = sl;
+        }
+        int v = (Lb + BS - 1) / BS;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int t = __shfl_up(v, off);
@@ -436,7 +453,16 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         int carry = 0;
         for (int base = 0; base < a.B; base += kThreads) {
             const int b = base + tid;
-            int v = b < a.B ? (clamp_len<BS>(a, b) + BS - 1) / BS : 0;
+            const int32_t *sp = a.k_new ? a.slots : a.lens;
+            const int bi = b < a.B ? b : 0;
+            const int rl = a.lens[bi], sr = sp[bi];
+            const int Lb = b < a.B ? clamp_raw_len<BS>(a, rl) : 0;
+            const int sl = a.k_new ? sr : -1;
+            if (b < a.B) {
+                lds_len[b] = Lb;
+                lds_slot[b] = sl;
+            }
+            int v = (Lb + BS - 1) / BS;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int t = __shfl_up(v, off);
@@ -494,7 +520,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         const int sb = lds_pref[b], se = lds_pref[b + 1];
         const int j0 = (int)(x - sb);
         const int j1 = (int)((end < se ? end : (int64_t)se) - sb);
-        const int L = clamp_len<BS>(a, b);
+        const int L = lds_len[b];
         const int nblk = se - sb;
         const int32_t *bt = a.tables + (int64_t)b * a.stride;
 
@@ -523,7 +549,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
             if (tid + kThreads < n0)
                 id1 = bt[j0 + tid + kThreads];
             if (last_piece) {
-                nslot = a.slots[b];
+                nslot = lds_slot[b];
                 if (tid < 2 * LPT)
                     nv = static_cast<const uint4 *>(tid < LPT ? a.k_new : a.v_new)
                         [((int64_t)b * a.Hkv + g) * LPT + tid % LPT];
@@ -751,7 +777,7 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     for (int i = tid; i < ndefer * 2 * LPT; i += kThreads) {
         const int k = i / (2 * LPT), u = i % (2 * LPT);
         const int bd = lds_defer[k];
-        const int nslot = a.slots[bd];
+        const int nslot = lds_slot[bd];
         const uint4 row = static_cast<const uint4 *>(u < LPT ? a.k_new : a.v_new)
             [((int64_t)bd * a.Hkv + g) * LPT + u % LPT];
         store_new_chunk(a, nslot, g, u / LPT, u % LPT, row);
