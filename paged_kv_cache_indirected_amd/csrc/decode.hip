@@ -65,6 +65,12 @@ constexpr int NW = 4;                 // waves per workgroup
 constexpr int kThreads = NW * 64;
 constexpr float kLazyMax = 8.0f;      // running-max slack, log2 units
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data format, no swizzle
+// Cache policy of the K/V tile loads: bit 1 of the buffer load's aux
+// operand, the non-temporal hint (nt).  Each tile is read once per call, so
+// the streaming hint keeps the tiles from displacing what is reused; the
+// Llama-70B-shaped call runs ~10% faster with it than with the default
+// policy (sc0 or sc1 alone change nothing).
+constexpr int kTilePolicy = 2;
 constexpr int kIdChunk = 2 * kThreads; // block-table entries staged in LDS at a time
 constexpr int kDefer = 64;            // fused-append rows a workgroup writes at its end
 
@@ -609,13 +615,13 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
             for (int kk = 0; kk < NKL; ++kk)
                 kr[kk] = __builtin_bit_cast(
                     uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rk, (int)(koff + (uint32_t)((4 * kk * BS + 16 * h) * 16)), 0, 0));
+                               rk, (int)(koff + (uint32_t)((4 * kk * BS + 16 * h) * 16)), 0, kTilePolicy));
 #pragma unroll
             for (int u = 0; u < NVL; ++u) {
                 const uint32_t c = DT == PKV_F32 ? (uint32_t)((4 * h * D + 16 * u) * 16)
                                                  : (uint32_t)((4 * h * D + 32 * u) * 8);
                 vr[u] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + c), 0, 0));
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + c), 0, kTilePolicy));
             }
         };
 
