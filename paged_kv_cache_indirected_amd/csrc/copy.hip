@@ -9,8 +9,12 @@
 // in each cache ([num_blocks][Hkv][BS][D]), so a pair is two plain
 // contiguous copies.  Workgroup x takes pair x / (2 * P), tensor
 // (x / P) % 2 and piece x % P of kPiece bytes; each thread moves kUnroll
-// 16-byte chunks, issuing every load before any store.  HBM bound: 2 * block
-// bytes read and written per pair.
+// 16-byte chunks, issuing every load before any store.  The loads carry the
+// non-temporal hint (each source byte is read once): 4096 random pairs of
+// 64 KiB blocks copy in ~0.085 ms instead of ~0.113 ms with the default
+// policy.  The stores keep the default policy: non-temporal stores slowed
+// copies into pinned host memory.  HBM bound: 2 * block bytes read and
+// written per pair.
 #include <hip/hip_runtime.h>
 
 #include "pkv_internal.h"
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void k_copy_blocks(
     for (int u = 0; u < kUnroll; ++u) {
         const int32_t o = base + u * kThreads * 16;
         if (o < block_bytes)
-            r[u] = *reinterpret_cast<const u32x4 *>(src + o);
+            r[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + o));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {

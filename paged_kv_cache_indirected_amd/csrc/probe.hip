@@ -14,7 +14,8 @@
 //                          (n * 16 bytes read, n * 16 written) against which
 //                          hardware byte counters are scaled.
 // Each reader folds what it loads into an XOR kept in one word per
-// workgroup so that no load can be dropped.
+// workgroup so that no load can be dropped.  The readers' loads carry the
+// non-temporal hint, as the decode's tile loads do (every byte is read once).
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4 *__restric
     uint32_t acc = 0;
     const size_t stride = (size_t)gridDim.x * kThreads;
     for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-        const uint4 v = src[i];
+        const uint4 v = __builtin_nontemporal_load(src + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     __shared__ uint32_t red[kThreads];
@@ -87,15 +88,15 @@ __global__ __launch_bounds__(kThreads) void k_tile_read(const char *__restrict__
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int cc = c + u < runs ? c + u : runs - 1;
-                    r[u] = *reinterpret_cast<const uint4 *>(k0 + cc * 1024);
-                    r[4 + u] = *reinterpret_cast<const uint4 *>(v0 + cc * 1024);
+                    r[u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(k0 + cc * 1024));
+                    r[4 + u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(v0 + cc * 1024));
                 }
                 if (pair) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int cc = c + u < runs ? c + u : runs - 1;
-                        r[8 + u] = *reinterpret_cast<const uint4 *>(k1 + cc * 1024);
-                        r[12 + u] = *reinterpret_cast<const uint4 *>(v1 + cc * 1024);
+                        r[8 + u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(k1 + cc * 1024));
+                        r[12 + u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(v1 + cc * 1024));
                     }
                 } else {
 #pragma unroll
