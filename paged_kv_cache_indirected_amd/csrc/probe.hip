@@ -25,13 +25,22 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A 16-byte load with the non-temporal hint.
+__device__ __forceinline__ uint4 nt_load16(const void *p)
+{
+    const u32x4 x = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4 *__restrict__ src, size_t n,
                                                           uint32_t *__restrict__ sink)
 {
     uint32_t acc = 0;
     const size_t stride = (size_t)gridDim.x * kThreads;
     for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-        const uint4 v = __builtin_nontemporal_load(src + i);
+        const uint4 v = nt_load16(src + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     __shared__ uint32_t red[kThreads];
@@ -88,15 +97,15 @@ __global__ __launch_bounds__(kThreads) void k_tile_read(const char *__restrict__
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int cc = c + u < runs ? c + u : runs - 1;
-                    r[u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(k0 + cc * 1024));
-                    r[4 + u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(v0 + cc * 1024));
+                    r[u] = nt_load16(k0 + cc * 1024);
+                    r[4 + u] = nt_load16(v0 + cc * 1024);
                 }
                 if (pair) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int cc = c + u < runs ? c + u : runs - 1;
-                        r[8 + u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(k1 + cc * 1024));
-                        r[12 + u] = __builtin_nontemporal_load(reinterpret_cast<const uint4 *>(v1 + cc * 1024));
+                        r[8 + u] = nt_load16(k1 + cc * 1024);
+                        r[12 + u] = nt_load16(v1 + cc * 1024);
                     }
                 } else {
 #pragma unroll
