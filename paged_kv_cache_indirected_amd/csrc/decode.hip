@@ -220,7 +220,6 @@ __device__ __forceinline__ int clamp_raw_len(const Args &a, int L)
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-
 // Balanced ranges.  Flattened block x of sequence b costs x + pc * b:
 // besides its blocks, a workgroup pays a fixed time at every sequence
 // boundary in its range (the load pipeline drains and refills, q and block
@@ -427,10 +426,11 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, n = lane & 15;
 
-    // Prefix sums of the per-sequence block counts (the same in every
-    // workgroup).  Up to 64 sequences every wave computes them alone and
-    // writes the whole table itself, so it reads it back with no barrier
-    // (the other waves write the same values).
+    // Prefix sums of the per-sequence block counts, and each sequence's
+    // clamped length and append slot for the piece set-up (the same in
+    // every workgroup).  Up to 64 sequences every wave computes them alone
+    // and writes the whole tables itself, so it reads them back with no
+    // barrier (the other waves write the same values).
     if (a.B <= 64) {
         // Both loads unconditional (sequence 0 for idle lanes; slots read
         // from the lengths when there is no fused append), so they are in
