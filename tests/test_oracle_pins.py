@@ -257,6 +257,73 @@ def test_prefill_zero_prior_first_row_is_v0():
     assert np.array_equal(out[0, 0], v0) and np.array_equal(out[0, 1], v0)
 
 
+# Several sequences in one call: priors 0, 7, 3, 12 and 2, chunks 5, 1, 0, 4
+# and 3 (a zero prior, a one-token chunk, an empty chunk between two
+# non-empty ones).  Every chunk row must attend exactly its own sequence's
+# keys 0 .. p0 + i ("Chunked prefill": splitting the prompt into chunks, and
+# batching chunks of several prompts in one step, leaves each row's result as
+# the unsplit prompt's).
+_MS_PRIOR, _MS_CHUNK = [0, 7, 3, 12, 2], [5, 1, 0, 4, 3]
+
+
+def _multi_seq_prefill(dtype):
+    return synth.custom_prefill(304, _MS_PRIOR, _MS_CHUNK, Hq=4, Hkv=2, D=8, block_size=16,
+                                dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_multi_sequence_rows_match_mpmath(dtype):
+    # Brute force at 50 digits for every row of every sequence, with the
+    # sequence, the row's position in its chunk and the key range worked out
+    # here from the chunk lengths (not from the oracle's row lookup).
+    pre = _multi_seq_prefill(dtype)
+    out = oracle.prefill(pre.q, pre.query_start, pre.k, pre.v, pre.lens, pre.shape.scale)
+    qf, kf, vf = _as_f64(pre.q), _as_f64(pre.k), _as_f64(pre.v)
+    G = pre.shape.Hq // pre.shape.Hkv
+    r, kv0 = 0, 0
+    for p0, C in zip(_MS_PRIOR, _MS_CHUNK):
+        for i in range(C):
+            keys = slice(kv0, kv0 + p0 + i + 1)
+            for h in range(pre.shape.Hq):
+                ref = _mp_attend(qf[r, h], kf[keys, h // G], vf[keys, h // G], pre.shape.scale)
+                assert np.max(np.abs(out[r, h] - np.array([float(x) for x in ref]))) <= 1e-13, \
+                    (r, h)
+            r += 1
+        kv0 += p0 + C
+    assert r == out.shape[0]
+
+
+def test_prefill_multi_sequence_rows_equal_single_sequence_decode():
+    # Row i of sequence b equals a one-sequence decode over that sequence's
+    # first p0 + i + 1 rows (the sequence's own K/V cut out here by hand).
+    pre = _multi_seq_prefill("bf16")
+    out = oracle.prefill(pre.q, pre.query_start, pre.k, pre.v, pre.lens, pre.shape.scale)
+    r, kv0 = 0, 0
+    for p0, C in zip(_MS_PRIOR, _MS_CHUNK):
+        for i in range(C):
+            L = p0 + i + 1
+            dec = oracle.decode(pre.q[r:r + 1], pre.k[kv0:kv0 + L], pre.v[kv0:kv0 + L], [L],
+                                pre.shape.scale)
+            assert np.array_equal(dec[0], out[r]), r
+            r += 1
+        kv0 += p0 + C
+
+
+def test_prefill_multi_sequence_rows_subset_matches_full():
+    # The row-subset path: each (row, head) pair computed alone equals the
+    # full call, for the first and last row of every non-empty chunk.
+    pre = _multi_seq_prefill("bf16")
+    full = oracle.prefill(pre.q, pre.query_start, pre.k, pre.v, pre.lens, pre.shape.scale)
+    qs = pre.query_start
+    rows = sorted({int(x) for b in range(len(_MS_CHUNK)) if qs[b + 1] > qs[b]
+                   for x in (qs[b], qs[b + 1] - 1)})
+    pairs = np.array([(r, h) for r in rows for h in range(pre.shape.Hq)], dtype=np.int32)
+    part = oracle.prefill(pre.q, pre.query_start, pre.k, pre.v, pre.lens, pre.shape.scale,
+                          rows=pairs)
+    for r, h in pairs:
+        assert np.array_equal(part[r, h], full[r, h])
+
+
 # --------------------------------------------------------------------------
 # Append: a tiny cache image written out by hand, plus invariants.
 
