@@ -25,11 +25,23 @@
  *   - Element types: q, k, v and the caches share one dtype (PKV_F32 or
  *     PKV_BF16); index arrays are int32.
  *
- * Cache layout (the pages fix none; this library's reading): each of
- * k_cache and v_cache is [num_blocks][num_kv_heads][block_size][head_dim]
- * elements, so one KV head's share of a block is one contiguous tile.  A slot
- * s names block s / block_size, offset s % block_size.  Query head h reads KV
- * head h / (num_q_heads / num_kv_heads).
+ * Cache layout (the pages fix none; this library's reading).  Each of
+ * k_cache and v_cache holds num_blocks x num_kv_heads tiles; tile (block b,
+ * KV head g) is one contiguous run of block_size * head_dim elements
+ * starting at element (b * num_kv_heads + g) * block_size * head_dim.  A slot
+ * s names block s / block_size, token offset s % block_size.  Inside a tile
+ * the elements are NOT row-major.  With bs = block_size, D = head_dim and
+ * E = 16 / element size (8 for bf16, 4 for f32), element (token t, dim d)
+ * sits at tile offset
+ *     K:  ((d / E) * bs + t) * E + d % E
+ *         (each token's dims in 16-byte chunks, chunk-major: chunk c of all
+ *         bs tokens, then chunk c + 1, ...)
+ *     V:  ((t / 4) * D + d) * 4 + t % 4
+ *         (4 consecutive tokens of one dim side by side, then the next dim)
+ * pkv_k_elem_offset / pkv_v_elem_offset below give the full element offset.
+ * pkv_append and pkv_append_decode write this layout; a cache filled any
+ * other way must follow it.  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads).
  */
 #ifndef PKV_H
 #define PKV_H
@@ -62,6 +74,23 @@ typedef struct pkv_cache_desc {
     int32_t head_dim;
     int32_t dtype;        /* PKV_F32 or PKV_BF16 */
 } pkv_cache_desc;
+
+/* Element offset of (block, KV head, token offset t, dim d) in k_cache,
+ * resp. v_cache, for the layout above (no range checks). */
+static inline int64_t pkv_k_elem_offset(const pkv_cache_desc *c, int32_t block, int32_t head,
+                                        int32_t t, int32_t d)
+{
+    const int64_t bs = c->block_size, D = c->head_dim;
+    const int64_t E = c->dtype == PKV_F32 ? 4 : 8;
+    return ((int64_t)block * c->num_kv_heads + head) * bs * D + ((d / E) * bs + t) * E + d % E;
+}
+static inline int64_t pkv_v_elem_offset(const pkv_cache_desc *c, int32_t block, int32_t head,
+                                        int32_t t, int32_t d)
+{
+    const int64_t bs = c->block_size, D = c->head_dim;
+    return ((int64_t)block * c->num_kv_heads + head) * bs * D + ((int64_t)(t / 4) * D + d) * 4 +
+           t % 4;
+}
 
 /* Static text for a return code. */
 const char *pkv_strerror(int code);

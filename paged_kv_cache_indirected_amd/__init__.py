@@ -147,8 +147,16 @@ def abi_version() -> int:
 
 @dataclass(frozen=True)
 class CacheDesc:
-    """Shape of one layer's cache: k_cache / v_cache are each
-    [num_blocks][num_kv_heads][block_size][head_dim] of ``dtype``."""
+    """Shape of one layer's cache.
+
+    k_cache / v_cache each hold num_blocks x num_kv_heads tiles of
+    block_size * head_dim elements of ``dtype`` (allocated here as
+    [num_blocks][num_kv_heads][block_size][head_dim] for the sizes only).
+    Inside a tile the order is not row-major: with E = 16 // element size,
+    K element (token t, dim d) sits at ((d // E) * block_size + t) * E + d % E
+    and V element (t, d) at ((t // 4) * head_dim + d) * 4 + t % 4 (the C
+    header's pkv_k_elem_offset / pkv_v_elem_offset).  pkv_append writes this
+    layout; fill a cache any other way only by the same offsets."""
     num_blocks: int
     num_kv_heads: int
     block_size: int

@@ -6,8 +6,8 @@
 //
 // Pair i copies block src_ids[i] of (src_k, src_v) to block dst_ids[i] of
 // (dst_k, dst_v).  A block is one contiguous run of Hkv * BS * D elements
-// in each cache ([num_blocks][Hkv][BS][D]), so a pair is two plain
-// contiguous copies.  Workgroup x takes pair x / (2 * P), tensor
+// in each cache (its Hkv tiles back to back, whatever the order inside a
+// tile), so a pair is two plain contiguous copies.  Workgroup x takes pair x / (2 * P), tensor
 // (x / P) % 2 and piece x % P of kPiece bytes; each thread moves kUnroll
 // 16-byte chunks, issuing every load before any store.  The loads carry the
 // non-temporal hint (each source byte is read once): 4096 random pairs of
