@@ -190,6 +190,28 @@ int pkv_decode(const void *q, const void *k_cache, const void *v_cache,
                const pkv_cache_desc *c, void *stream);
 
 /* ------------------------------------------------------------------------
+ * pkv_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, computation and result as pkv_decode with the same
+ * num_splits (bit for bit), without the workspace: the split partials live
+ * in a scratch area inside the library, PKV_DECODE_NOALLOC_SCRATCH_BYTES on
+ * each GPU it runs on, held until the process ends.  A call whose partials
+ * need more (pkv_decode_workspace_bytes(...) above the limit) returns
+ * PKV_EINVAL; pkv_decode with a caller workspace has no such limit.  The
+ * scratch address is looked up once per device, on the first call with that
+ * device current.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (two streams, two host threads) race and give
+ * wrong results; order them.  Nothing needs clearing between calls.
+ */
+#define PKV_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int pkv_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, int32_t block_table_stride,
+                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+                       int32_t num_splits, const pkv_cache_desc *c, void *stream);
+
+/* ------------------------------------------------------------------------
  * Decode step with the append fused into the same launch.
  *
  * Same result, cache contents included, as

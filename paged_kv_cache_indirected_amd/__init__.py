@@ -71,6 +71,8 @@ _sig("pkv_decode_num_splits", _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _DESC)
 _sig("pkv_decode", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, ctypes.c_float, _P,
      _i32, _i32, _P, _sz, _DESC, _P)
+_sig("pkv_decode_noalloc", ctypes.c_int, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32,
+     ctypes.c_float, _P, _i32, _i32, _DESC, _P)
 _sig("pkv_append_decode", ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32,
      ctypes.c_float, _P, _i32, _i32, _P, _sz, _DESC, _P)
 _sig("pkv_prefill_workspace_bytes", _sz, _i32, _i32, _i32, _DESC)
@@ -289,6 +291,34 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, d
                          int(num_splits), _dev(workspace, "workspace"), ws_bytes,
                          ctypes.byref(desc.c()), _stream(stream))
     _check(rc, "pkv_decode")
+
+
+# Bytes of partials pkv_decode_noalloc can hold (PKV_DECODE_NOALLOC_SCRATCH_BYTES).
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                   desc: CacheDesc, max_context_len: int, num_splits: int = 0,
+                   stream=None) -> None:
+    """pkv_decode_noalloc: pkv_decode without a workspace, for callers
+    that cannot allocate; the split partials live in the library's per-GPU
+    scratch (calls that overlap on one GPU race)."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    _need(D == desc.head_dim and _dtype_code(q) == desc.dtype, "q must be [B][Hq][head_dim]")
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] >= B, "block_tables must be [B][W]")
+    _need(context_lens.numel() >= B, "context_lens must hold B entries")
+    _cache_ok(k_cache, desc, "k_cache")
+    _cache_ok(v_cache, desc, "v_cache")
+    rc = _lib.pkv_decode_noalloc(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                 _dev(block_tables, "block_tables", torch.int32),
+                                 int(block_tables.shape[1]),
+                                 _dev(context_lens, "context_lens", torch.int32), B, Hq,
+                                 int(max_context_len), float(scale), _dev(out, "out"),
+                                 _dtype_code(out), int(num_splits), ctypes.byref(desc.c()),
+                                 _stream(stream))
+    _check(rc, "pkv_decode_noalloc")
 
 
 def append_decode(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,

@@ -223,7 +223,7 @@ int decode_call(const char *who, const void *q, const void *k_cache, const void 
                 int32_t max_context_len, float scale, void *out, int32_t out_dtype,
                 int32_t num_splits, void *workspace, size_t workspace_bytes,
                 const pkv_cache_desc *c, void *stream, const void *k_new, const void *v_new,
-                const int32_t *slots, float *lse = nullptr)
+                const int32_t *slots, float *lse = nullptr, bool launch = true)
 {
     int rc = check_desc(c, who);
     if (rc || (rc = check_heads(num_q_heads, c, who)))
@@ -266,6 +266,8 @@ int decode_call(const char *who, const void *q, const void *k_cache, const void 
     if (workspace_bytes < lay.total)
         return fail(PKV_EINVAL, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
                     lay.total);
+    if (!launch)
+        return PKV_OK;
     pkv::DecodeLaunch d{};
     d.q = q;
     d.k_cache = k_cache;
@@ -342,6 +344,45 @@ extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cach
                        context_lens, num_seqs, num_q_heads, max_context_len, scale, out, out_dtype,
                        num_splits, workspace, workspace_bytes, c, stream, nullptr, nullptr,
                        nullptr);
+}
+
+extern "C" int pkv_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, int32_t block_table_stride,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len, float scale,
+                                  void *out, int32_t out_dtype, int32_t num_splits,
+                                  const pkv_cache_desc *c, void *stream)
+{
+    static const char *who = "pkv_decode_noalloc";
+    pkv::clear_error();
+    int rc = check_desc(c, who);
+    if (rc || (rc = check_heads(num_q_heads, c, who)))
+        return rc;
+    if (num_seqs > 0 && num_splits >= 0 && num_splits <= 65535) {
+        const int32_t W = num_splits > 0 ? num_splits : auto_splits(num_seqs, max_context_len, c);
+        const size_t need = ws_layout(num_seqs, num_q_heads, W, c->head_dim).total;
+        if (need > PKV_DECODE_NOALLOC_SCRATCH_BYTES)
+            return fail(PKV_EINVAL,
+                        "%s: %d sequences x %d query heads with %d splits need %zu bytes of "
+                        "partials, above the %zu-byte no-allocation scratch; use pkv_decode with "
+                        "a workspace", who, num_seqs, num_q_heads, W, need,
+                        (size_t)PKV_DECODE_NOALLOC_SCRATCH_BYTES);
+    }
+    // Every host-side check first (a stand-in workspace pointer that is never
+    // used), so that a rejected call touches no device state.
+    alignas(16) static char stand_in;
+    rc = decode_call(who, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                     num_seqs, num_q_heads, max_context_len, scale, out, out_dtype, num_splits,
+                     &stand_in, PKV_DECODE_NOALLOC_SCRATCH_BYTES, c, stream, nullptr, nullptr,
+                     nullptr, nullptr, false);
+    if (rc || num_seqs == 0)
+        return rc;
+    void *ws = nullptr;
+    if ((rc = pkv::decode_noalloc_scratch(&ws)))
+        return rc;
+    return decode_call(who, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                       num_seqs, num_q_heads, max_context_len, scale, out, out_dtype, num_splits,
+                       ws, PKV_DECODE_NOALLOC_SCRATCH_BYTES, c, stream, nullptr, nullptr, nullptr);
 }
 
 extern "C" int pkv_append_decode(const void *k_new, const void *v_new,

@@ -56,7 +56,15 @@
 //     land on one XCD and blocks shared between sequences stay in its L2.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "pkv_internal.h"
+
+// Split partials of pkv_decode_noalloc (callers that cannot allocate device
+// memory).  Each GPU the library runs on holds its own copy until the
+// process ends; in host code the name is only a handle for the symbol
+// lookup in decode_noalloc_scratch(), never a device address.
+static __device__ __align__(256) unsigned char scratch[PKV_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace pkv {
 namespace {
@@ -990,6 +998,34 @@ int32_t device_cu_count()
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+int decode_noalloc_scratch(void **ptr)
+{
+    // The address of the current device's copy of `scratch`, looked up once
+    // per device with that device current, then reused.
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();
+        return fail(PKV_EHIP, "pkv_decode_noalloc: no current device (%s)", hipGetErrorString(e));
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(PKV_EHIP, "pkv_decode_noalloc: scratch lookup on device %d failed: %s",
+                        dev, hipGetErrorString(e));
+        }
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return PKV_OK;
 }
 
 int32_t decode_piece_cost(int32_t block_size, int32_t head_dim, int32_t elem_size)

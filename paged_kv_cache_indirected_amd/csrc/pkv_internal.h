@@ -50,6 +50,9 @@ struct DecodeLaunch {
     float *lse = nullptr;      // optional [B][Hq] log2-sum-exp of the scaled scores
 };
 int launch_decode(const DecodeLaunch &a);
+// Device address of the current device's pkv_decode_noalloc scratch
+// (PKV_DECODE_NOALLOC_SCRATCH_BYTES), looked up on the first call per device.
+int decode_noalloc_scratch(void **ptr);
 // Cost of a sequence boundary in a decode workgroup's range, in blocks.
 int32_t decode_piece_cost(int32_t block_size, int32_t head_dim, int32_t elem_size);
 // out[r][d] = sum_k o[k][r][d] 2^(lse[k][r] - M) / sum_k 2^(lse[k][r] - M),

@@ -214,3 +214,40 @@ def test_prefill_workspace_sizes_key_split_states():
     assert L.pkv_prefill_workspace_bytes(1, 64, 64, ctypes.byref(_desc(dtype=pkv.F32))) == 0
     assert L.pkv_prefill_workspace_bytes(1, 64, 64, ctypes.byref(_desc(head_dim=96))) == 0
     assert L.pkv_prefill_workspace_bytes(0, 64, 64, ctypes.byref(d)) == 0
+
+
+def _decode_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, stride=8, lens=FAKE, B=2, Hq=64, maxL=100,
+             scale=0.1, out=FAKE, odt=pkv.F32, pt=0, desc=_desc())
+    a.update(kw)
+    return L.pkv_decode_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["stride"], a["lens"], a["B"],
+                                a["Hq"], a["maxL"], a["scale"], a["out"], a["odt"], a["pt"],
+                                ctypes.byref(a["desc"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), pkv.EINVAL),
+    (dict(out=MIS), pkv.EINVAL),
+    (dict(Hq=128), pkv.EUNSUPPORTED),
+    (dict(maxL=16 * 8 + 1), pkv.EINVAL),
+    (dict(pt=-1), pkv.EINVAL),
+    (dict(odt=3), pkv.EINVAL),
+    (dict(B=600), pkv.EINVAL),        # partials beyond the no-allocation scratch
+    (dict(B=2, pt=4000), pkv.EINVAL),  # likewise, through the split count
+])
+def test_decode_noalloc_rejects(kw, code):
+    # Rejected on the host, before any device call (none is possible here).
+    assert _decode_noalloc(**kw) == code
+    assert pkv._lib.pkv_last_error().decode() != ""
+
+
+def test_decode_noalloc_limit_matches_header():
+    src = open(HEADER).read()
+    assert "#define PKV_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in src
+    assert pkv.DECODE_NOALLOC_SCRATCH_BYTES == 16 << 20
+    d = _desc()
+    # The largest batch that fits at the library's split for 64 query heads.
+    fits = [B for B in (1, 32, 256, 400, 600, 1024)
+            if L.pkv_decode_workspace_bytes(B, 64, 100, 0, ctypes.byref(d)) <= 16 << 20]
+    assert 32 in fits and 256 in fits and 600 not in fits
+    assert _decode_noalloc(B=0, q=None, out=None) == pkv.OK
