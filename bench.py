@@ -37,6 +37,8 @@ METRIC = "paged decode effective KV GB/s (% of HBM peak) + seq-steps/s, 64q/8kv 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_cfg2_pmc_traffic.json")
+PMC_INDIRECTION_FILE = os.path.join(ROOT, "profiles", "decode_cfg2_indirection_pmc.json")
+PMC_CFG4_FILE = os.path.join(ROOT, "profiles", "decode_cfg4_pmc_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_indirected_amd", "csrc", "decode.hip")
 
 
@@ -68,6 +70,23 @@ class Timer:
             evs[i][1].record()
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3   # seconds
+
+    def amortized(self, fn, n, warmup=3):
+        """Seconds per call over n back-to-back calls bracketed by one pair
+        of events (the launch overhead of each call overlaps the previous
+        call's execution, as in a serving loop)."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
 
 
 def paged_state(batch, pool_seed, device="cuda"):
@@ -146,17 +165,22 @@ def cpu_baseline(batch, min_seconds: float = 10.0, max_reps: int = 400):
             "seq_steps_per_s": round(batch.B * reps / el, 2)}
 
 
-def pmc_traffic(launch_bytes):
-    """HBM bytes per decode call from the committed PMC summary, if it was
-    taken on the current decode source; else None."""
+def _pmc_record(path):
+    """A committed PMC summary, if it was taken on the current decode source
+    (its decode.hip SHA-256 matches); else None."""
     try:
-        rec = json.load(open(PMC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if rec.get("decode_hip_sha256") != sha:
-        return None
-    return rec.get("hbm_bytes_per_call")
+    return rec if rec.get("decode_hip_sha256") == sha else None
+
+
+def pmc_traffic(launch_bytes):
+    """HBM bytes per decode call from the committed PMC summary, if it was
+    taken on the current decode source; else None."""
+    rec = _pmc_record(PMC_FILE)
+    return None if rec is None else rec.get("hbm_bytes_per_call")
 
 
 # ---------------------------------------------------------------------------
@@ -207,6 +231,133 @@ def bench_tile_probe(lib, sink, states, sh, kv_bytes, timer, grid=256):
     return round(kv_bytes / float(np.median(t)) / 1e9, 1)
 
 
+def identity_states(batch, copies):
+    """Paged copies of a decode batch whose sequences' rows are appended
+    whole, in order, from an ascending free list: each sequence's blocks are
+    consecutive and ascending (the placement a contiguous per-sequence cache
+    would have)."""
+    import paged_kv_cache_indirected_amd as pkv
+    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    sh = batch.shape
+    out = []
+    for _ in range(copies):
+        c = PagedCache(batch.pool_blocks, sh.Hkv, sh.block_size, sh.D, pkv.BF16, pool_seed=0)
+        ids = list(range(batch.B))
+        c.add_sequences(ids, batch.lens, batch.k, batch.v)
+        tables, lens, mx = c.tables(ids)
+        tab = tables.cpu().numpy()
+        for b in range(batch.B):
+            nb = (int(batch.lens[b]) + sh.block_size - 1) // sh.block_size
+            assert np.all(np.diff(tab[b, :nb]) == 1), "identity placement is not contiguous"
+        out.append(dict(cache=c, tables=tables, lens=lens, max_len=mx,
+                        q=to_device_rows(batch.q, pkv.BF16, "cuda")))
+    return out
+
+
+def bench_indirection(timer, batch, shuffled, splits, calls=200):
+    """The cost of the logical-to-physical block map: the Llama-70B-shaped
+    decode call over the same rows placed in shuffled blocks (the
+    headline's copies) and in an identity placement (every sequence's
+    blocks consecutive and ascending: what a contiguous per-sequence cache
+    would read), the same number of copies rotated for each.  HBM bytes per
+    call by counter come from the committed summary when it matches the
+    decode source."""
+    import paged_kv_cache_indirected_amd as pkv
+    sh = batch.shape
+    identity = identity_states(batch, len(shuffled))
+    max_len = max(s["max_len"] for s in shuffled + identity)
+    desc = shuffled[0]["cache"].desc
+    ws = workspace(batch.B, sh.Hq, max_len, desc, splits)
+    import torch
+    res_out = torch.empty((batch.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+    kv = float(batch.lens.sum()) * kv_row_bytes(sh)
+
+    def timed(states):
+        it = [0]
+
+        def call():
+            st = states[it[0] % len(states)]
+            it[0] += 1
+            c = st["cache"]
+            pkv.decode(st["q"], c.k_cache, c.v_cache, st["tables"], st["lens"], sh.scale,
+                       res_out, c.desc, max_len, workspace=ws, num_splits=splits)
+        return timer.per_call(call, calls, warmup=10)
+    ts, ti = [], []
+    for _ in range(2):                       # alternate: drift hits both alike
+        ts.append(timed(shuffled))
+        ti.append(timed(identity))
+    t_s = float(np.median(np.concatenate(ts)))
+    t_i = float(np.median(np.concatenate(ti)))
+    r = {"workload": "the Llama-70B-shaped decode call (B=32, 64q/8kv, d128, bf16, block 16) "
+                     "over shuffled blocks vs an identity placement (each sequence's blocks "
+                     f"consecutive), {len(shuffled)} copies of each rotated",
+         "shuffled_ms": round(1e3 * t_s, 5), "identity_ms": round(1e3 * t_i, 5),
+         "shuffled_GBps": round(kv / t_s / 1e9, 1), "identity_GBps": round(kv / t_i / 1e9, 1),
+         "shuffled_over_identity_time": round(t_s / t_i, 4)}
+    rec = _pmc_record(PMC_INDIRECTION_FILE)
+    if rec is not None:
+        r["hbm_fetch_bytes_per_call"] = {"shuffled": rec["shuffled_fetch_bytes_per_call"],
+                                         "identity": rec["identity_fetch_bytes_per_call"]}
+    del identity
+    return r
+
+
+def bench_metadata(timer, batch, steps=50):
+    """Per-step metadata of the Llama-70B-shaped step (a2): the host
+    bookkeeping (one new token per sequence, then block tables and lengths)
+    written into pinned memory, and its one asynchronous copy to the device,
+    each timed alone (the GPU idle), beside the decode step's kernel time."""
+    import torch
+    import paged_kv_cache_indirected_amd as pkv
+    from paged_kv_cache_indirected_amd.paged import StepMetadata
+    sh = batch.shape
+    st = paged_state(batch, batch.pool_seed)
+    cache = st["cache"]
+    ids = list(range(batch.B))
+    stride = int(st["tables"].shape[1]) + (steps + sh.block_size) // sh.block_size + 1
+    md = StepMetadata(batch.B, stride, depth=4)
+    host_s, h2d_s = [], []
+    ids = np.arange(batch.B, dtype=np.int64)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for i in range(steps + 5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h = md.fill(cache.seqs, ids)
+        t1 = time.perf_counter()
+        md.upload(h, timing=ev)
+        torch.cuda.synchronize()
+        if i >= 5:
+            host_s.append(t1 - t0)
+            h2d_s.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+    nbytes = 4 * batch.B * (stride + 2)
+    del st
+    return {"workload": f"decode-step metadata of B={batch.B} sequences: slots, context lengths "
+                        f"and block tables ({stride} entries per row), pinned host -> device",
+            "bytes_per_step": nbytes,
+            "host_bookkeeping_us": round(1e6 * float(np.median(host_s)), 2),
+            "h2d_us": round(1e6 * float(np.median(h2d_s)), 2),
+            "note": "outside the kernels' timed region; a serving loop overlaps the copy with "
+                    "the previous step's kernels (non-blocking, stream-ordered)"}
+
+
+def cpu_single_thread(batch, min_seconds: float = 3.0):
+    """The oracle on one host thread, whole decode step, repeated until
+    min_seconds have elapsed (at least once)."""
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(batch.q, batch.k, batch.v, batch.lens, batch.shape.scale, threads=1)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    step_bytes = float(batch.lens.sum()) * kv_row_bytes(batch.shape)
+    return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "seq_steps_per_s": round(batch.B * reps / el, 2),
+            "sample": f"{batch.name}: whole decode step (B={batch.B}, "
+                      f"{int(batch.lens.sum())} context tokens) x {reps} in {el:.1f} s"}
+
+
 def bench_cfg3(timer, steps, splits):
     """Continuous-batching steps: 256 sequences, 32-token blocks; each step
     appends one token per sequence and decodes; between steps 10% of the
@@ -214,7 +365,7 @@ def bench_cfg3(timer, steps, splits):
     import torch
     import paged_kv_cache_indirected_amd as pkv
     import synth
-    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
+    from paged_kv_cache_indirected_amd.paged import PagedCache, StepMetadata, to_device_rows
     b0 = synth.cfg3_initial()
     sh = b0.shape
     st = b0.seq_start()
@@ -230,11 +381,22 @@ def bench_cfg3(timer, steps, splits):
     out = torch.empty((b0.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
     ws = workspace(b0.B, sh.Hq, stride * sh.block_size, cache.desc, splits)
     times, times_fused, kvb = [], [], 0.0
+    md = StepMetadata(b0.B, stride, depth=4)
+    md_host, md_h2d = [], []
+    md_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for step in range(1, steps + 1):
-        slots = torch.from_numpy(cache.seqs.append_batch(ids)).to("cuda")
         kn, vn, qn = synth.cfg3_step_rows(step, b0.B, sh)
         kn, vn, qn = (to_device_rows(x, pkv.BF16, "cuda") for x in (kn, vn, qn))
-        tab, lens, mx = cache.tables(ids, stride)
+        # The step's metadata: bookkeeping into pinned memory, one async copy
+        # (each timed alone here; a serving loop overlaps the copy with the
+        # previous step's kernels).
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h = md.fill(cache.seqs, ids)
+        md_host.append(time.perf_counter() - t0)
+        tab, lens, slots, mx = md.upload(h, timing=md_ev)
+        torch.cuda.synchronize()
+        md_h2d.append(md_ev[0].elapsed_time(md_ev[1]) * 1e-3)
 
         def run():
             pkv.append(kn, vn, slots, cache.k_cache, cache.v_cache, cache.desc)
@@ -265,7 +427,13 @@ def bench_cfg3(timer, steps, splits):
             "steps": steps, "ms_per_step": round(1e3 * t / steps, 4),
             "kv_GBps": round(kvb / t / 1e9, 1),
             "seq_steps_per_s": round(b0.B * steps / t, 1),
-            "pct_of_hbm_peak": round(100 * kvb / t / 1e9 / HBM_PEAK_GBS, 2)}
+            "pct_of_hbm_peak": round(100 * kvb / t / 1e9 / HBM_PEAK_GBS, 2),
+            "metadata": {"bytes_per_step": 4 * b0.B * (stride + 2),
+                         "host_bookkeeping_us": round(1e6 * float(np.median(md_host)), 2),
+                         "h2d_us": round(1e6 * float(np.median(md_h2d)), 2),
+                         "note": "slots, context lengths and block tables written by the host "
+                                 "bookkeeping into pinned memory and copied asynchronously; "
+                                 "outside the step's timed kernels"}}
 
 
 def bench_decode_sweep(timer):
@@ -313,14 +481,21 @@ def bench_decode_sweep(timer):
                 pkv.decode(st["q"], c.k_cache, c.v_cache, st["tables"], st["lens"], sh.scale, out,
                            desc, L, workspace=ws, num_splits=W)
             t = float(np.median(timer.per_call(call, max(2 * R, 40), warmup=R)))
+            ta = timer.amortized(call, max(4 * R, 200), warmup=R)
             entry[label] = {"ms": round(1e3 * t, 4), "kv_GBps": round(kv / t / 1e9, 1),
-                            "pct_of_hbm_peak": round(100 * kv / t / 1e9 / HBM_PEAK_GBS, 2)}
+                            "pct_of_hbm_peak": round(100 * kv / t / 1e9 / HBM_PEAK_GBS, 2),
+                            "ms_back_to_back": round(1e3 * ta, 4),
+                            "pct_of_hbm_peak_back_to_back":
+                                round(100 * kv / ta / 1e9 / HBM_PEAK_GBS, 2)}
         entry["split_speedup"] = round(entry["one_wg_per_seq"]["ms"] / entry["auto_split"]["ms"], 3)
         res[f"B{B}"] = entry
         del states
         torch.cuda.empty_cache()
     res["workload"] = ("decode at B = 1..128, every context 4096, 64q/8kv, d128, bf16, block 16: "
                        "automatic split vs one workgroup per (sequence, KV head)")
+    res["timing"] = ("ms: median of single calls, each bracketed by its own events; "
+                     "ms_back_to_back: events around a run of back-to-back calls over the "
+                     "rotated copies, per call")
     return res
 
 
@@ -371,6 +546,10 @@ def bench_cfg4(timer, splits):
             "cascade_ms_per_call": round(1e3 * tc, 4),
             "cascade_unique_kv_GBps": round(unique / tc / 1e9, 1),
             "cascade_speedup": round(t / tc, 3),
+            "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+            "hbm_bytes_by_counter": (lambda r: None if r is None else {
+                "plain": r["plain_hbm_bytes_per_call"],
+                "cascade": r["cascade_hbm_bytes_per_call"]})(_pmc_record(PMC_CFG4_FILE)),
             "note": "logical bytes read the shared prefix once per sequence; repeated prefix "
                     "tiles are served from L2/Infinity Cache, so logical GB/s can exceed HBM"}
 
@@ -810,6 +989,85 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_path, 
     print(json.dumps(rec))
 
 
+def _pmc_calls(csv_path, counter, kernels, skip=1):
+    """Per-call sums of a counter over the listed kernels (KiB): dispatch
+    i of each kernel belongs to call i; the first `skip` calls (warm-up,
+    cold caches) are dropped."""
+    per = [_pmc_per_dispatch(csv_path, k, counter) for k in kernels]
+    n = min(len(x) for x in per)
+    return [sum(x[i] for x in per) for i in range(skip, n)]
+
+
+def _copy_scale(copy_csv, counter, nbytes=1 << 30):
+    return nbytes / (1024.0 * float(np.median(_pmc_per_dispatch(copy_csv, "k_copy", counter))))
+
+
+def pmc_summary_indirection(id_csv, sh_csv, copy_fetch_csv):
+    """FETCH_SIZE per decode call (k_decode + k_merge) for the identity and
+    the shuffled placement, scaled by the copy probe's factor."""
+    import synth
+    b = synth.cfg2()
+    sf = _copy_scale(copy_fetch_csv, "FETCH_SIZE")
+    ident = 1024.0 * sf * float(np.mean(_pmc_calls(id_csv, "FETCH_SIZE", ["k_decode", "k_merge"])))
+    shuf = 1024.0 * sf * float(np.mean(_pmc_calls(sh_csv, "FETCH_SIZE", ["k_decode", "k_merge"])))
+    rec = {"kernel": "pkv_decode call on the Llama-70B-shaped batch (k_decode + k_merge), "
+                     "identity vs shuffled block placement",
+           "decode_hip_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+           "fetch_scale": sf,
+           "identity_fetch_bytes_per_call": ident, "shuffled_fetch_bytes_per_call": shuf,
+           "algorithmic_bytes_per_call": float(b.lens.sum()) * kv_row_bytes(b.shape)}
+    with open(PMC_INDIRECTION_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def pmc_summary_cfg4(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per call of the prefix-sharing workload by counter: the
+    plain decode (k_decode + k_merge, the calls before the cascade's first
+    prefill-kernel dispatch) and the cascade decode (suffix k_decode +
+    k_merge, prefix k_prefill, k_merge_states)."""
+    import csv as _csv
+    import synth
+    sf = _copy_scale(copy_fetch_csv, "FETCH_SIZE")
+    sw = _copy_scale(copy_write_csv, "WRITE_SIZE")
+
+    def split(path, counter):
+        rows = {}
+        for r in _csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                d = int(r["Dispatch_Id"])
+                rows.setdefault(d, [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+        order = sorted(rows)
+        first_pf = next(d for d in order if "k_prefill" in rows[d][0])
+        plain_dec = [rows[d][1] for d in order if d < first_pf and "k_decode" in rows[d][0]]
+        plain_mrg = [rows[d][1] for d in order if d < first_pf and "k_merge<" in rows[d][0]]
+        cas = [rows[d] for d in order if d >= first_pf - 2]
+        names = ("k_decode", "k_merge<", "k_prefill", "k_merge_states")
+        cas_sum = {n: [v for k, v in cas if n in k] for n in names}
+        ncall = min(len(x) for x in cas_sum.values())
+        plain = float(np.mean([a + m for a, m in zip(plain_dec[3:], plain_mrg[3:])]))
+        casc = float(np.mean([sum(cas_sum[n][i] for n in names) for i in range(3, ncall)]))
+        return plain, casc
+    pf, cf = split(fetch_csv, "FETCH_SIZE")
+    pw, cw = split(write_csv, "WRITE_SIZE")
+    b = synth.cfg4()
+    row = kv_row_bytes(b.shape)
+    rec = {"kernel": "prefix-sharing decode, 128 sequences on one 2048-token prefix: plain "
+                     "pkv_decode (k_decode + k_merge) and pkv_decode_cascade (k_decode + k_merge "
+                     "+ k_prefill + k_merge_states)",
+           "decode_hip_sha256": hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest(),
+           "fetch_scale": sf, "write_scale": sw,
+           "plain_hbm_bytes_per_call": 1024.0 * (sf * pf + sw * pw),
+           "cascade_hbm_bytes_per_call": 1024.0 * (sf * cf + sw * cw),
+           "plain_fetch_bytes_per_call": 1024.0 * sf * pf,
+           "cascade_fetch_bytes_per_call": 1024.0 * sf * cf,
+           "logical_kv_bytes": float(b.lens.sum()) * row,
+           "unique_kv_bytes": float(b.prefix_len + (b.lens - b.prefix_len).sum()) * row}
+    with open(PMC_CFG4_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -831,7 +1089,22 @@ def main():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                        "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn counter CSVs into the committed per-call traffic summary")
+    ap.add_argument("--indirection-pmc", choices=["identity", "shuffled"],
+                    help="run only the Llama-70B-shaped decode call on one placement "
+                         "(for a hardware-counter run)")
+    ap.add_argument("--pmc-summary-indirection", nargs=3,
+                    metavar=("IDENTITY_FETCH_CSV", "SHUFFLED_FETCH_CSV", "COPY_FETCH_CSV"),
+                    help="turn the two placements' FETCH_SIZE CSVs into the committed summary")
+    ap.add_argument("--pmc-summary-cfg4", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn counter CSVs of '--only prefix_sharing' into the committed summary")
     args = ap.parse_args()
+    if args.pmc_summary_indirection:
+        pmc_summary_indirection(*args.pmc_summary_indirection)
+        return
+    if args.pmc_summary_cfg4:
+        pmc_summary_cfg4(*args.pmc_summary_cfg4)
+        return
     if args.pmc_summary:
         import synth
         b = synth.cfg2()
@@ -865,6 +1138,23 @@ def main():
         return
     batch = synth.cfg2()
     sh = batch.shape
+    if args.indirection_pmc:
+        if args.indirection_pmc == "identity":
+            sts = identity_states(batch, args.copies)
+        else:
+            sts = [paged_state(batch, batch.pool_seed + 7919 * r) for r in range(args.copies)]
+        mx = max(s["max_len"] for s in sts)
+        ws = workspace(batch.B, sh.Hq, mx, sts[0]["cache"].desc, args.splits)
+        o = torch.empty((batch.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+        for i in range(args.warmup + args.steps):
+            s = sts[i % len(sts)]
+            c = s["cache"]
+            pkv.decode(s["q"], c.k_cache, c.v_cache, s["tables"], s["lens"], sh.scale, o, c.desc,
+                       mx, workspace=ws, num_splits=args.splits)
+        torch.cuda.synchronize()
+        print(json.dumps({"indirection_pmc": args.indirection_pmc, "calls": args.steps,
+                          "warmup": args.warmup}))
+        return
     log(f"[bench] building {args.copies} paged copies of the Llama-70B-shaped batch "
         f"(B={batch.B}, sum L={int(batch.lens.sum())}, pool={batch.pool_blocks} blocks)")
     states = [paged_state(batch, batch.pool_seed + 7919 * r) for r in range(args.copies)]
@@ -989,10 +1279,16 @@ def main():
         res["roofline"]["achievable_probes"] = probes
         res["roofline"]["frac_of_paged_tile_probe"] = round(
             gbs_dec / probes["paged_tile_read_GBps"], 4)
+        log("[bench] cost of indirection (identity vs shuffled placement)")
+        indirection = bench_indirection(timer, batch, states, args.splits)
         del states
         torch.cuda.empty_cache()
+        log("[bench] step metadata (pinned host -> device)")
+        metadata = bench_metadata(timer, batch)
+        torch.cuda.empty_cache()
         log("[bench] continuous batching")
-        wl = {"continuous_batching": bench_cfg3(timer, 10, args.splits)}
+        wl = {"indirection": indirection, "metadata_h2d": metadata}
+        wl["continuous_batching"] = bench_cfg3(timer, 10, args.splits)
         torch.cuda.empty_cache()
         log("[bench] prefix sharing")
         wl["prefix_sharing"] = bench_cfg4(timer, args.splits)
@@ -1018,6 +1314,9 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(batch)
+        log("[bench] timing the CPU oracle on one thread (tiny and Llama-70B-shaped steps)")
+        res["cpu_baseline"]["one_thread"] = {"tiny_f32_d64": cpu_single_thread(synth.cfg1()),
+                                             "llama70b_shaped": cpu_single_thread(batch, 1.0)}
     print(json.dumps(res), flush=True)
 
 

@@ -511,11 +511,16 @@ class Seqs:
                "pkv_seqs_append")
         return out[:n]
 
-    def append_batch(self, seq_ids):
-        """One token for each listed sequence; returns the slots."""
+    def append_batch(self, seq_ids, out=None):
+        """One token for each listed sequence; returns the slots.  ``out``:
+        an optional contiguous int32 array of at least len(seq_ids) entries
+        (e.g. a view of pinned host memory) that receives them."""
         import numpy as np
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
-        out = np.empty(max(len(ids), 1), dtype=np.int32)
+        if out is None:
+            out = np.empty(max(len(ids), 1), dtype=np.int32)
+        _need(out.dtype == np.int32 and out.flags.c_contiguous and out.size >= len(ids),
+              "out must be a contiguous int32 array of len(seq_ids) entries")
         _check(_lib.pkv_seqs_append_batch(self._h, len(ids), ids.ctypes.data, out.ctypes.data),
                "pkv_seqs_append_batch")
         return out[:len(ids)]
@@ -614,12 +619,21 @@ class Seqs:
         _lib.pkv_seqs_block_ids(self._h, int(seq_id), n, buf)
         return list(buf[:n])
 
-    def fill(self, seq_ids, stride: int):
-        """Block tables [n][stride] (padding -1) and context lengths [n], int32."""
+    def fill(self, seq_ids, stride: int, out=None):
+        """Block tables [n][stride] (padding -1) and context lengths [n], int32.
+        ``out``: optional (tables, lens) contiguous int32 arrays to fill
+        (e.g. views of pinned host memory)."""
         import numpy as np
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
-        tables = np.empty((len(ids), int(stride)), dtype=np.int32)
-        lens = np.empty(max(len(ids), 1), dtype=np.int32)
+        if out is None:
+            tables = np.empty((len(ids), int(stride)), dtype=np.int32)
+            lens = np.empty(max(len(ids), 1), dtype=np.int32)
+        else:
+            tables, lens = out
+            _need(tables.dtype == np.int32 and lens.dtype == np.int32 and
+                  tables.flags.c_contiguous and lens.flags.c_contiguous and
+                  tables.size >= len(ids) * int(stride) and lens.size >= len(ids),
+                  "out must be contiguous int32 (tables [n][stride], lens [n]) arrays")
         _check(_lib.pkv_seqs_fill(self._h, len(ids), ids.ctypes.data, tables.ctypes.data,
                                   int(stride), lens.ctypes.data), "pkv_seqs_fill")
         return tables, lens[:len(ids)]

@@ -38,6 +38,79 @@ def to_device_rows(rows: np.ndarray, code: int, device) -> torch.Tensor:
     return t.to(device, non_blocking=False)
 
 
+class StepMetadata:
+    """A decode step's metadata -- block tables, context lengths and the
+    slots of the step's new tokens -- written by the host bookkeeping straight
+    into pinned host memory and copied to the device with one asynchronous
+    copy on the caller's stream ("LLM Inference: KV Cache, Batching &
+    Scheduling", "PagedAttention and vLLM": the logical-to-physical map is
+    kept by a host memory manager and changes every step).
+
+    A ring of ``depth`` pinned buffers, each with its own device buffer: a
+    pinned buffer is refilled only once the copy that last read it has
+    completed (an event per buffer), so the host may run up to ``depth``
+    steps ahead of the GPU.  A device buffer is overwritten only by a copy
+    enqueued on the same stream after the kernels of the step that used it
+    (stream order); steps staged with one StepMetadata must use one stream.
+    """
+
+    def __init__(self, max_seqs: int, stride: int, depth: int = 4, device="cuda"):
+        self.max_seqs, self.stride = int(max_seqs), int(stride)
+        n = self.max_seqs * (self.stride + 2)
+        self.device = torch.device(device)
+        self.host = [torch.empty(n, dtype=torch.int32).pin_memory() for _ in range(depth)]
+        self.hostv = [h.numpy() for h in self.host]
+        self.dev = [torch.empty(n, dtype=torch.int32, device=self.device) for _ in range(depth)]
+        self.events = [torch.cuda.Event() for _ in range(depth)]
+        self.pending = [False] * depth
+        self.i = 0
+
+    def fill(self, seqs, seq_ids, append: bool = True):
+        """Host part: the step's bookkeeping for ``seq_ids`` (one new token
+        per sequence when ``append``: pkv_seqs_append_batch), then its block
+        tables and lengths (pkv_seqs_fill), written into the next pinned
+        buffer.  Returns a handle for upload()."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        B, W = len(ids), self.stride
+        if B > self.max_seqs:
+            raise ValueError(f"{B} sequences, room for {self.max_seqs}")
+        k = self.i
+        self.i = (self.i + 1) % len(self.host)
+        if self.pending[k]:
+            self.events[k].synchronize()
+        hv = self.hostv[k]
+        lens = hv[B:2 * B]
+        if append:
+            seqs.append_batch(ids, out=hv[:B])
+        seqs.fill(ids, W, out=(hv[2 * B:2 * B + B * W], lens))
+        return (k, B, append, int(lens.max()) if B else 0)
+
+    def upload(self, handle, stream=None, timing=None):
+        """Device part: one non-blocking copy of the filled buffer on
+        ``stream`` (default: the current stream).  ``timing``: an optional
+        pair of timing events recorded right before and after the copy.
+        Returns device (tables [B][stride], lens [B], slots [B] or None) and
+        the host maximum length."""
+        k, B, append, max_len = handle
+        W = self.stride
+        used = 2 * B + B * W
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(st):
+            if timing:
+                timing[0].record(st)
+            self.dev[k][:used].copy_(self.host[k][:used], non_blocking=True)
+            if timing:
+                timing[1].record(st)
+            self.events[k].record(st)
+        self.pending[k] = True
+        d = self.dev[k]
+        return (d[2 * B:used].view(B, W), d[B:2 * B], d[:B] if append else None, max_len)
+
+    def stage(self, seqs, seq_ids, append: bool = True, stream=None):
+        """fill() then upload()."""
+        return self.upload(self.fill(seqs, seq_ids, append), stream)
+
+
 class PagedCache:
     """One layer's paged K/V cache plus its host-side block bookkeeping."""
 
