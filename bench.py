@@ -1272,10 +1272,11 @@ def main():
         log("[bench] probes")
         probes, plib, sink = bench_probes(timer)
         probes["paged_tile_read_GBps"] = bench_tile_probe(plib, sink, states, sh, kv_bytes, timer)
-        probes["paged_tile_note"] = ("the decode's tiles of the same shuffled pools, read with "
-                                     "its access shape (one workgroup per CU, each wave a "
-                                     "contiguous run of the tile list, two tiles in flight) and "
-                                     "no arithmetic")
+        probes["paged_tile_note"] = ("the decode's 4 KiB (block, KV head) tiles of the same "
+                                     "shuffled pools, K and V, no arithmetic: one workgroup per "
+                                     "CU, each wave a contiguous run of the tile list (the 8 KV "
+                                     "heads of a block back to back; 1, 2 or 4 heads per run read "
+                                     "alike), two tiles in flight")
         res["roofline"]["achievable_probes"] = probes
         res["roofline"]["frac_of_paged_tile_probe"] = round(
             gbs_dec / probes["paged_tile_read_GBps"], 4)

@@ -418,6 +418,21 @@ int32_t blocks_needed(const Seq &q, int32_t bs, int32_t n)
     return (int32_t)std::max<int64_t>(0, need - (int64_t)q.blocks.size());
 }
 
+// The first id listed more than once in ids[0..n), or -1 (a sorted copy:
+// O(n log n) for the batch of a decode step).
+int64_t first_duplicate(int32_t n, const int64_t *ids, bool *found)
+{
+    std::vector<int64_t> v(ids, ids + n);
+    std::sort(v.begin(), v.end());
+    for (int32_t i = 1; i < n; ++i)
+        if (v[i] == v[i - 1]) {
+            *found = true;
+            return v[i];
+        }
+    *found = false;
+    return -1;
+}
+
 // Appending into the partially filled last block is only allowed when that
 // block is private.
 bool writes_shared_block(const pkv_seqs *s, const Seq &q, int32_t n)
@@ -467,6 +482,10 @@ extern "C" int pkv_seqs_append_batch(pkv_seqs *s, int32_t n, const int64_t *ids,
 {
     if (!s || n < 0 || (n > 0 && (!ids || !slots)))
         return fail(PKV_EINVAL, "pkv_seqs_append_batch: bad arguments");
+    bool dup = false;
+    const int64_t d = first_duplicate(n, ids, &dup);
+    if (dup)
+        return fail(PKV_EINVAL, "pkv_seqs_append_batch: sequence %lld listed twice", (long long)d);
     std::vector<Seq *> qs(n);
     int32_t total = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -474,10 +493,6 @@ extern "C" int pkv_seqs_append_batch(pkv_seqs *s, int32_t n, const int64_t *ids,
         if (it == s->seqs.end())
             return fail(PKV_ESTATE, "pkv_seqs_append_batch: unknown sequence %lld",
                         (long long)ids[i]);
-        for (int32_t j = 0; j < i; ++j)
-            if (ids[j] == ids[i])
-                return fail(PKV_EINVAL, "pkv_seqs_append_batch: sequence %lld listed twice",
-                            (long long)ids[i]);
         qs[i] = &it->second;
         if (qs[i]->swapped())
             return fail(PKV_ESTATE, "pkv_seqs_append_batch: sequence %lld is swapped out",
@@ -552,6 +567,11 @@ extern "C" int pkv_seqs_append_batch_cow(pkv_seqs *s, int32_t n, const int64_t *
 {
     if (!s || n < 0 || (n > 0 && (!ids || !slots || !copy_src || !copy_dst)) || !num_copies)
         return fail(PKV_EINVAL, "pkv_seqs_append_batch_cow: bad arguments");
+    bool dup = false;
+    const int64_t d = first_duplicate(n, ids, &dup);
+    if (dup)
+        return fail(PKV_EINVAL, "pkv_seqs_append_batch_cow: sequence %lld listed twice",
+                    (long long)d);
     std::vector<Seq *> qs(n);
     std::unordered_map<int32_t, int32_t> sharers;   // shared partial last block -> batch sharers
     int32_t total = 0;
@@ -560,10 +580,6 @@ extern "C" int pkv_seqs_append_batch_cow(pkv_seqs *s, int32_t n, const int64_t *
         if (it == s->seqs.end())
             return fail(PKV_ESTATE, "pkv_seqs_append_batch_cow: unknown sequence %lld",
                         (long long)ids[i]);
-        for (int32_t j = 0; j < i; ++j)
-            if (ids[j] == ids[i])
-                return fail(PKV_EINVAL, "pkv_seqs_append_batch_cow: sequence %lld listed twice",
-                            (long long)ids[i]);
         qs[i] = &it->second;
         if (qs[i]->swapped())
             return fail(PKV_ESTATE, "pkv_seqs_append_batch_cow: sequence %lld is swapped out",

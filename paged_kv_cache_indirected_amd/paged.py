@@ -64,6 +64,12 @@ class StepMetadata:
         self.events = [torch.cuda.Event() for _ in range(depth)]
         self.pending = [False] * depth
         self.i = 0
+        # One copy from every pinned buffer now: the first transfer out of a
+        # freshly pinned buffer pays a one-time mapping cost that would
+        # otherwise land on the first steps.
+        for h, d in zip(self.host, self.dev):
+            d.copy_(h, non_blocking=True)
+        torch.cuda.current_stream(self.device).synchronize()
 
     def fill(self, seqs, seq_ids, append: bool = True):
         """Host part: the step's bookkeeping for ``seq_ids`` (one new token

@@ -168,3 +168,20 @@ def test_fragmentation_stats():
     s.append(1, 17)
     st = s.stats()
     assert st["blocks_in_use"] == 2 and st["slots_unused"] == 15 and st["tokens"] == 17
+
+
+@pytest.mark.parametrize("cow", [False, True])
+def test_batch_append_rejects_a_sequence_listed_twice(cow):
+    # A decode step gives each sequence one token; a repeated id is a caller
+    # error, refused before anything changes.
+    pool = pkv.Pool(64, 3)
+    s = pkv.Seqs(pool, 4)
+    for i in range(40):
+        s.add(i)
+        s.append(i, 3)
+    free, lens = pool.num_free, [s.length(i) for i in range(40)]
+    batch = list(range(40)) + [17]
+    with pytest.raises(pkv.PkvError) as e:
+        (s.append_batch_cow if cow else s.append_batch)(batch)
+    assert e.value.code == pkv.EINVAL and "17" in str(e.value)
+    assert pool.num_free == free and [s.length(i) for i in range(40)] == lens
