@@ -15,10 +15,10 @@
 //   * 4 waves x 32 rows (NCT = 2 column tiles of 16; 48 rows per wave need
 //     more than half the register file, and one wave per SIMD ran 1.6x
 //     slower).  Keys are processed in tiles of 64.  The workgroup stages
-//     each tile of K ([64][D], row-major) and V (in the cache's order: 4
-//     consecutive keys of a dim together) into LDS from the paged cache with
-//     coalesced 16-byte loads (1 KiB runs of a block's tile), double buffered:
-//     the next tile's global loads are in flight while the current tile is
+//     each tile of K ([64][D], row-major) and V (per dim, the 8 keys of one
+//     PV operand side by side) into LDS from the paged cache with coalesced
+//     16-byte loads (1 KiB runs of a block's tile), double buffered: the
+//     next tile's global loads are in flight while the current tile is
 //     computed.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's
 //     Q rows held in registers for the whole kernel).  Computing the
@@ -63,14 +63,14 @@ constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data forma
 template <int D>
 struct PShape {
     static constexpr int KSTR = D + 8;               // LDS row stride of K (elements)
-    static constexpr int VGS = 4 * D + 64;           // LDS stride of a 4-key V group (elements)
+    static constexpr int VPS = 8 * D;                // LDS stride of a V group pair (elements)
     static constexpr int KBUF = KT * KSTR;
-    static constexpr int VBUF = (KT / 4) * VGS;
+    static constexpr int VBUF = (KT / 8) * VPS;
     static constexpr int NDS = D / 32;               // k-steps of S^T over head_dim
     static constexpr int NDT = D / 16;               // 16-row tiles of O^T
     static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
     static constexpr int KLD = KT * CPR / kThreads;  // K chunks staged per thread
-    static constexpr int VK = KT * CPR / kThreads;   // V keys staged per thread
+    static constexpr int VK = KT * CPR / kThreads;   // V 16-byte units staged per thread
     static_assert(KLD * kThreads == KT * CPR && (VK == 2 || VK == 4), "staging shape");
 };
 
@@ -112,6 +112,12 @@ __device__ __forceinline__ uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum): gfx950 has it as a
+// 3-input instruction that needs no quieting of its inputs, unlike fmaxf.
+// A NaN score can only come from a NaN in the attended keys or the query,
+// where the result is NaN either way (masked scores are -inf, never NaN).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Combine v with lane (l ^ X) (X = 16 or 32) by max; both lanes get the
 // same bits.
 template <int X>
@@ -120,7 +126,7 @@ __device__ __forceinline__ float xmax(float v)
     const uint32_t u = __builtin_bit_cast(uint32_t, v);
     auto p = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
                      : __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+    return vmax(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
 }
 template <int X>
 __device__ __forceinline__ float xsum(float v)
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
     using Sh = PShape<D>;
     constexpr int TQ = ROWS / G;                     // chunk tokens per workgroup
     constexpr int NDS = Sh::NDS, NDT = Sh::NDT, CPR = Sh::CPR, VK = Sh::VK;
-    constexpr int KSTR = Sh::KSTR, VGS = Sh::VGS;
+    constexpr int KSTR = Sh::KSTR, VPS = Sh::VPS;
     constexpr int IDS = kIdChunk;                    // block ids staged per chunk
     constexpr int CT = IDS * BS / KT;                // key tiles per id chunk
 
@@ -254,18 +260,32 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
     };
 
     uint4 kst[Sh::KLD], vst[VK];
-    // Global loads of key tile kt into registers.  Wave w reads part wp of
-    // block w / WPB of the tile (WPB = waves per block), one 1 KiB run of the
-    // block's (block, head) tile per load: K keeps each token's dims in
-    // 16-byte chunks (chunk c of token t at (c * BS + t) * 16 bytes), V
+    // Global loads of key tile kt into registers.  K: wave w reads part wp
+    // of block w / WPB of the tile (WPB = waves per block), one 1 KiB run of
+    // the block's (block, head) tile per load; K keeps each token's dims in
+    // 16-byte chunks (chunk c of token t at (c * BS + t) * 16 bytes).  V
     // keeps 4 consecutive tokens of one dim together (element (t, d) at
-    // ((t / 4) * D + d) * 4 + t % 4).  Each load goes through a buffer
-    // resource on the wave's block held in scalar registers; a block id
-    // outside the pool, or a block past the context, gets an empty resource
-    // and reads zeros without touching memory.
+    // ((t / 4) * D + d) * 4 + t % 4, a 4-key group being one 8 D-byte run),
+    // and is read in pairs of groups: pair pr = 4 s2 + qd holds the groups of
+    // keys 32 s2 + 16 h + 4 qd .. + 3 for h = 0, 1, the two halves of one PV
+    // operand.  Wave w reads pairs 2 w and 2 w + 1 (so s2 = w / 2), each lane
+    // the same 16-byte unit (2 dims x 4 keys) of both groups of a pair, so
+    // that it can store both halves of a dim side by side.  Each load goes
+    // through a buffer resource on the wave's block held in scalar registers;
+    // a block id outside the pool, or a block past the context, gets an
+    // empty resource and reads zeros without touching memory.
     constexpr int WPB = NW * BS / KT;                // waves per block of the tile
     const int wblk = BS * (w / WPB);                 // the wave's first key in the tile
     const int wp = w % WPB;
+    static_assert(VK * 64 == 2 * D, "two V group pairs per wave");
+    const int vs2 = w / 2;
+    int vquad[VK / 2], vu[VK / 2];
+#pragma unroll
+    for (int j = 0; j < VK / 2; ++j) {
+        const int cid = (w * (VK / 2) + j) * 64 + lane;
+        vquad[j] = (cid / (D / 2)) % 4;
+        vu[j] = cid % (D / 2);
+    }
     auto tile_rsrc = [&](const uint16_t *base, int j) {
         const int jj = __builtin_amdgcn_readfirstlane(j);
         const int id = jj < L ? lds_ids[(jj / BS) % IDS] : -1;
@@ -281,33 +301,36 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
         for (int i = 0; i < Sh::KLD; ++i)
             kst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rk, ((wp * Sh::KLD + i) * 64 + lane) * 16, 0, 0));
-        const auto rv = tile_rsrc(vg, kt * KT + wblk);
 #pragma unroll
-        for (int e = 0; e < VK; ++e)
-            vst[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rv, ((wp * VK + e) * 64 + lane) * 16, 0, 0));
+        for (int h = 0; h < 2; ++h) {
+            const auto rv = tile_rsrc(vg, kt * KT + 32 * vs2 + (BS == 16 ? 16 * h : 0));
+#pragma unroll
+            for (int j = 0; j < VK / 2; ++j)
+                vst[2 * j + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rv, (BS == 16 ? vquad[j] : 4 * h + vquad[j]) * 8 * D + vu[j] * 16, 0, 0));
+        }
         // Unused slots past the context end must not reach the PV product as
         // NaN (0 * NaN = NaN): zero them (only the tile holding the end).
         if (kt * KT + KT > L) {
 #pragma unroll
-            for (int e = 0; e < VK; ++e) {
-                const int q = (wp * VK + e) * 64 + lane;     // 16-byte unit of the V tile
-                const int nv = L - (kt * KT + wblk + 4 * ((2 * q) / D));
-                const uint32_t m01 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
-                const uint32_t m23 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
-                vst[e].x &= m01;
-                vst[e].y &= m23;
-                vst[e].z &= m01;
-                vst[e].w &= m23;
-            }
+            for (int j = 0; j < VK / 2; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int nv = L - (kt * KT + 32 * vs2 + 16 * h + 4 * vquad[j]);
+                    const uint32_t m01 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+                    const uint32_t m23 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+                    uint4 &x = vst[2 * j + h];
+                    x.x &= m01;
+                    x.y &= m23;
+                    x.z &= m01;
+                    x.w &= m23;
+                }
         }
     };
-    // Registers -> LDS buffer: K rows as they are; V in the cache's own
-    // order, 4-key groups of [D][4] (group gi of the tile at gi * VGS, the
-    // 128-byte pad putting consecutive groups on opposite halves of the
-    // banks), so every store is a contiguous 16-byte run.  16-byte unit q of
-    // the wave's K part is chunk q / BS of token q % BS; unit q of its V part
-    // holds tokens 4 (2q / D) .. + 3 of dims 2 (q % (D / 2)) and the next.
+    // Registers -> LDS buffer: K rows as they are (16-byte unit q of the
+    // wave's K part is chunk q / BS of token q % BS); V as [pair][D][8]: the
+    // 4 keys of dim d from the pair's first group, then its 4 keys from the
+    // second, so one 16-byte LDS read is one PV operand.
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < Sh::KLD; ++i) {
@@ -316,11 +339,11 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
             *reinterpret_cast<uint4 *>(&lds_k[buf][kk * KSTR + cc * 8]) = kst[i];
         }
 #pragma unroll
-        for (int e = 0; e < VK; ++e) {
-            const int q = (wp * VK + e) * 64 + lane;
-            const int gi = wblk / 4 + (2 * q) / D;
-            const int d0 = 2 * (q % (D / 2));
-            *reinterpret_cast<uint4 *>(&lds_v[buf][gi * VGS + d0 * 4]) = vst[e];
+        for (int j = 0; j < VK / 2; ++j) {
+            uint16_t *v0 = &lds_v[buf][(4 * vs2 + vquad[j]) * VPS + 2 * vu[j] * 8];
+            const uint4 a = vst[2 * j], b = vst[2 * j + 1];
+            *reinterpret_cast<uint4 *>(v0) = make_uint4(a.x, a.y, b.x, b.y);
+            *reinterpret_cast<uint4 *>(v0 + 8) = make_uint4(a.z, a.w, b.z, b.w);
         }
     };
 
@@ -394,11 +417,12 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
         float alpha[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            float mt = -INFINITY;
+            // Max of the lane's 16 scores, two new values per 3-input step.
+            float mt = vmax(sacc[0][ct][0], vmax(sacc[0][ct][1], sacc[0][ct][2]));
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                mt = fmaxf(mt, fmaxf(fmaxf(sacc[ks][ct][0], sacc[ks][ct][1]),
-                                     fmaxf(sacc[ks][ct][2], sacc[ks][ct][3])));
+            for (int k = 3; k < 15; k += 2)
+                mt = vmax(mt, vmax(sacc[k / 4][ct][k % 4], sacc[(k + 1) / 4][ct][(k + 1) % 4]));
+            mt = vmax(mt, sacc[3][ct][3]);
             mt = xmax<16>(mt);
             mt = xmax<32>(mt) * c;
             const bool up = mt > m[ct] + kLazyMax;
@@ -458,13 +482,11 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             // A operand of dims dt*16 + n: k slots 8 quad + 4 half + i hold key
-            // 32 s2 + 16 half + 4 quad + i (the order of P^T's B operand), i.e.
-            // the 4 keys of dim d in groups 8 s2 + quad and 8 s2 + 4 + quad.
+            // 32 s2 + 16 half + 4 quad + i (the order of P^T's B operand): dim
+            // d of V group pair 4 s2 + quad.
             auto vload = [&](int dt) {
-                const uint16_t *v0 = &lds_v[buf][(8 * s2 + quad) * VGS + (dt * 16 + n) * 4];
-                const uint2 lo = *reinterpret_cast<const uint2 *>(v0);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(v0 + 4 * VGS);
-                return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                return *reinterpret_cast<const bf16x8 *>(
+                    &lds_v[buf][(4 * s2 + quad) * VPS + (dt * 16 + n) * 8]);
             };
             bf16x8 vprev = vload(0);
 #pragma unroll
