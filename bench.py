@@ -89,6 +89,43 @@ class Timer:
         return a.elapsed_time(b) * 1e-3 / n
 
 
+def decode_side_bytes(lens, sh, splits, out_bytes=4):
+    """Bytes a pkv_decode call moves besides the K/V rows (the algorithmic
+    bytes): q rows, the output, block-table entries and context lengths, and
+    the split pieces' partial states (written by the split pass, read by the
+    merge).  The pieces follow the split pass's cut: a cost line of
+    blocks + piece_cost per sequence boundary cut into `splits` equal ranges
+    per KV head; a sequence whose blocks span several ranges leaves one
+    partial (G x (D + 2) floats) per range and KV head."""
+    bs, D, Hq, Hkv = sh.block_size, sh.D, sh.Hq, sh.Hkv
+    esz = 4 if sh.dtype == "f32" else 2
+    G = Hq // Hkv
+    L = np.asarray(lens, dtype=np.int64)
+    nb = (L + bs - 1) // bs
+    pref = np.concatenate([[0], np.cumsum(nb)])
+    B, T = len(L), int(pref[-1])
+    pc = max(1, 147456 // (2 * bs * D * esz))
+    Ct = T + pc * B
+
+    def owner(c):
+        return ((c + 1) * splits + Ct - 1) // Ct - 1
+    pieces = 0
+    for b in range(B):
+        sb, se = int(pref[b]), int(pref[b + 1])
+        if se > sb:
+            wf, wl = owner(sb + pc * b), owner(se - 1 + pc * b)
+            pieces += (wl - wf + 1) if wl > wf else 0
+    part = pieces * Hkv * G * (D + 2) * 4
+    side = {"q": B * Hq * D * esz, "out": B * Hq * D * out_bytes,
+            "block_tables": T * 4 * Hkv, "context_lens_and_prefix_sums": B * 4 + 2 * (B + 1) * 4,
+            "partials_written": part, "partials_read": part}
+    side["total"] = int(sum(side.values()))
+    side["split_pieces_per_kv_head"] = pieces
+    side["note"] = ("block-table entries counted once per KV head (each head's workgroups read "
+                    "their ranges' ids); partial states of sequences cut between workgroups")
+    return side
+
+
 def paged_state(batch, pool_seed, device="cuda"):
     """One paged copy of a decode batch: every row but each sequence's last
     loaded through the pool and pkv_append; the step's last token is left for
@@ -742,6 +779,24 @@ def bench_append(timer):
         res[label] = {"rows": T, "ms_per_call": round(1e3 * t, 4),
                       "GBps_read_plus_write": round(nbytes / t / 1e9, 1),
                       "frac_of_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        if T <= 4096:
+            # A call this small is shorter than its host-side launch path:
+            # also time 64 calls captured in one HIP graph and replayed.
+            n_rep = 64
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                pkv.append(k, v, sl, kc, vc, desc)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=st):
+                for _ in range(n_rep):
+                    pkv.append(k, v, sl, kc, vc, desc)
+            tg = timer.amortized(graph.replay, 10, warmup=2) / n_rep
+            res[label].update({"ms_per_call_graph_replay": round(1e3 * tg, 4),
+                               "GBps_graph_replay": round(nbytes / tg / 1e9, 1),
+                               "note": "ms_per_call: each call event-timed alone (host "
+                                       "launch path included); graph replay: 64 calls back "
+                                       "to back on the device"})
     res["workload"] = ("pkv_append: rows [T][8][128] bf16 into a 16384-block cache, slots random "
                        "and distinct, or whole blocks in order (prefill chunks), or one row per "
                        "sequence for 256 sequences (a decode step)")
@@ -1283,8 +1338,13 @@ def main():
             "avg_launch_ms": round(1e3 * dec_avg, 5),
             "p10_ms": round(1e3 * float(np.percentile(dec_s, 10)), 5),
             "p90_ms": round(1e3 * float(np.percentile(dec_s, 90)), 5),
+            "side_bytes_per_launch": decode_side_bytes(batch.lens, sh, splits),
         },
     }
+    side = res["roofline"]["side_bytes_per_launch"]
+    if res["roofline"]["traffic"]:
+        res["roofline"]["traffic_over_algorithmic_plus_side"] = round(
+            res["roofline"]["traffic"] / (kv_bytes + side["total"]), 4)
     if not args.headline_only:
         log("[bench] probes")
         probes, plib, sink = bench_probes(timer)
