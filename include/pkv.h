@@ -252,6 +252,14 @@ int pkv_append_decode(const void *k_new, const void *v_new, const int32_t *slot_
  * arguments as pkv_decode (max_context_len bounds context_lens); the
  * workspace (size from pkv_decode_cascade_workspace_bytes) needs no
  * initialisation, and calls sharing one must not overlap.
+ *
+ * Streams: the suffix decode runs on `stream`; the prefix pass runs beside
+ * it on a stream the library creates once per device (default priority,
+ * non-blocking), which first waits for all work enqueued on `stream` before
+ * the call, and `stream` then waits for it before the state merge.  To the
+ * caller the call is ordered on `stream` like any other, also under HIP
+ * graph capture (the side branch is captured through the two events).
+ * Host threads calling it on one device are serialised while they enqueue.
  */
 size_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                           int32_t prefix_len, int32_t max_context_len,

@@ -22,7 +22,7 @@ PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")   # measurement probes, loaded 
 OBJ = os.path.join(ROOT, "_build", "pkv")
 
 HOST_SRC = ["errors.cpp", "pool.cpp", "sched.cpp", "api.cpp"]
-HIP_SRC = ["append.hip", "copy.hip", "decode.hip", "prefill.hip"]
+HIP_SRC = ["append.hip", "copy.hip", "decode.hip", "prefill.hip", "side_stream.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 vector ops are switched off for all device code.

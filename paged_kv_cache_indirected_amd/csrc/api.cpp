@@ -461,32 +461,40 @@ extern "C" int pkv_decode_cascade(const void *q, const void *k_cache, const void
     float *o_all = reinterpret_cast<float *>(ws + lay.o);
     float *lse_all = reinterpret_cast<float *>(ws + lay.lse);
     // The suffixes: a plain split decode writing a normalised fp32 state.
-    rc = decode_call(who, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
-                     num_seqs, num_q_heads, max_context_len, scale,
-                     o_all + (size_t)ks * rows * c->head_dim, PKV_F32, W, ws + lay.dws,
-                     workspace_bytes - lay.dws, c, stream, nullptr, nullptr, nullptr,
-                     lse_all + (size_t)ks * rows);
-    if (rc != PKV_OK)
-        return rc;
-    if (ks > 0) {
-        // The shared prefix once for all sequences: ks pseudo-sequences, one
-        // per range of prefix blocks, each holding every sequence's queries
-        // (read from the same rows) and attending its whole range; the
-        // kernel derives each one's query rows and key count itself.
+    auto suffixes = [&](void *st) {
+        return decode_call(who, q, k_cache, v_cache, block_tables, block_table_stride,
+                           context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                           o_all + (size_t)ks * rows * c->head_dim, PKV_F32, W, ws + lay.dws,
+                           workspace_bytes - lay.dws, c, st, nullptr, nullptr, nullptr,
+                           lse_all + (size_t)ks * rows);
+    };
+    // The shared prefix once for all sequences: ks pseudo-sequences, one per
+    // range of prefix blocks, each holding every sequence's queries (read
+    // from the same rows) and attending its whole range; the kernel derives
+    // each one's query rows and key count itself.
+    auto prefix = [&](void *st) {
         const int32_t nbk = (nb + ks - 1) / ks;
         pkv::PrefillLaunch p{q, nullptr, ks, num_seqs, k_cache, v_cache, prefix_blocks, nbk,
                              nullptr, nbk * c->block_size, num_q_heads, c->num_kv_heads,
                              c->num_blocks, c->block_size, c->head_dim, scale, o_all, PKV_F32,
-                             stream};
+                             st};
         p.causal = 0;
         p.q_shared = 1;
         p.lse = lse_all;
         p.syn_rows = num_seqs;
         p.syn_nbk = nbk;
         p.syn_nb = nb;
-        if ((rc = pkv::launch_prefill(p)))
-            return rc;
-    }
+        return pkv::launch_prefill(p);
+    };
+    // The two passes write disjoint states and read only q and the caches:
+    // the suffix decode (HBM-bound, the longer one) is launched first on the
+    // caller's stream and the prefix pass (MFMA-bound) beside it on the
+    // library's side stream, so that they share the CUs.  On 128 sequences
+    // over a 2048-token prefix, calls back to back: 69-71 us against
+    // 76-77 us one after the other.
+    rc = ks > 0 ? pkv::launch_forked(stream, suffixes, prefix) : suffixes(stream);
+    if (rc != PKV_OK)
+        return rc;
     return pkv::launch_merge_states(o_all, lse_all, ks + 1, rows, c->head_dim, out, out_dtype,
                                     stream);
 }

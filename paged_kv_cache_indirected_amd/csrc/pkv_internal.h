@@ -3,6 +3,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <functional>
 
 #include "pkv.h"
 
@@ -53,6 +54,14 @@ int launch_decode(const DecodeLaunch &a);
 // Device address of the current device's pkv_decode_noalloc scratch
 // (PKV_DECODE_NOALLOC_SCRATCH_BYTES), looked up on the first call per device.
 int decode_noalloc_scratch(void **ptr);
+// Runs on_main(stream) and on_side(side) so that the two may execute
+// concurrently: the side stream (one per device, the library's) first waits
+// for everything enqueued on `stream` so far, and `stream` then waits for
+// everything launched on the side stream, so later work on `stream` sees
+// both.  Host callers on one device are serialised for the sequence.
+// Returns the first failing branch's code (the join is enqueued anyway).
+int launch_forked(void *stream, const std::function<int(void *)> &on_main,
+                  const std::function<int(void *)> &on_side);
 // Cost of a sequence boundary in a decode workgroup's range, in blocks.
 int32_t decode_piece_cost(int32_t block_size, int32_t head_dim, int32_t elem_size);
 // out[r][d] = sum_k o[k][r][d] 2^(lse[k][r] - M) / sum_k 2^(lse[k][r] - M),

@@ -82,8 +82,8 @@ def _shared_batch(seed, B, P, own, Hq, Hkv, D, bs):
     (9, 16 * 33, [1] * 9, 1, 128, 16),
     (40, 16 * 64, list(range(40)), 8, 128, 16),
     (2, 32, [0, 0], 2, 64, 32),
-    # More sequences than one decode launch holds (1024): the prefix pass
-    # then runs before the suffix launches, each merging its own sequences.
+    # More sequences than one decode launch holds (1024): the suffix
+    # launches, each merging its own sequences, run beside the prefix pass.
     (1100, 16 * 4, [i % 5 for i in range(1100)], 1, 64, 16),
 ])
 def test_cascade_shapes(B, P, own, G, D, bs):
