@@ -1120,16 +1120,21 @@ def pmc_summary_cfg4(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
                 d = int(r["Dispatch_Id"])
                 rows.setdefault(d, [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
         order = sorted(rows)
-        first_pf = next(d for d in order if "k_prefill" in rows[d][0])
-        plain_dec = [rows[d][1] for d in order if d < first_pf and "k_decode" in rows[d][0]]
-        plain_mrg = [rows[d][1] for d in order if d < first_pf and "k_merge<" in rows[d][0]]
-        cas = [rows[d] for d in order if d >= first_pf - 2]
-        names = ("k_decode", "k_merge<", "k_prefill", "k_merge_states")
-        cas_sum = {n: [v for k, v in cas if n in k] for n in names}
-        ncall = min(len(x) for x in cas_sum.values())
-        plain = float(np.mean([a + m for a, m in zip(plain_dec[3:], plain_mrg[3:])]))
-        casc = float(np.mean([sum(cas_sum[n][i] for n in names) for i in range(3, ncall)]))
-        return plain, casc
+        kind = [("dec" if "k_decode" in rows[d][0] else "mrg" if "k_merge<" in rows[d][0] else
+                 "pf" if "k_prefill" in rows[d][0] else "ms" if "k_merge_states" in rows[d][0]
+                 else "other") for d in order]
+        val = [rows[d][1] for d in order]
+        # A cascade call is the suffix k_decode + k_merge, the prefix
+        # k_prefill and k_merge_states, enqueued in that order; a plain
+        # call is a k_decode + k_merge pair with no k_prefill after it.
+        plain, casc = [], []
+        for i in range(len(order)):
+            if kind[i] == "ms" and i >= 3 and kind[i - 3:i] == ["dec", "mrg", "pf"]:
+                casc.append(sum(val[i - 3:i + 1]))
+            elif (kind[i] == "dec" and i + 1 < len(order) and kind[i + 1] == "mrg" and
+                  (i + 2 >= len(order) or kind[i + 2] != "pf")):
+                plain.append(val[i] + val[i + 1])
+        return float(np.mean(plain[3:])), float(np.mean(casc[3:]))
     pf, cf = split(fetch_csv, "FETCH_SIZE")
     pw, cw = split(write_csv, "WRITE_SIZE")
     b = synth.cfg4()
