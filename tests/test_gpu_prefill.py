@@ -170,3 +170,27 @@ def test_repeat_is_bitwise_deterministic():
     o1 = run_prefill(*st, b.shape.scale, 128)
     o2 = run_prefill(*st, b.shape.scale, 128)
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_out_of_range_block_id_reads_zeros(split):
+    # A block id outside the pool inside the context (a precondition
+    # violation) is read as zero keys and values, never from memory: the
+    # oracle gets zeros for those rows.
+    b = synth.custom_prefill(315, prior=[200, 40], chunk=[48, 32], Hq=16, Hkv=2, D=128,
+                             block_size=16)
+    cache, q, qs, tables, lens, mx = prefill_state(b)
+    bs = b.shape.block_size
+    k, v = b.k.copy(), b.v.copy()
+    start = np.concatenate([[0], np.cumsum(b.lens)])
+    for s, j, bad in ((0, 3, cache.desc.num_blocks + 5), (0, 9, -3), (1, 1, 1 << 30)):
+        tables[s, j] = bad
+        r0 = start[s] + j * bs
+        k[r0:r0 + bs] = 0
+        v[r0:r0 + bs] = 0
+    C = int(b.chunk.max())
+    out = run_prefill(cache, q, qs, tables, lens, mx, b.shape.scale, C, split=split)
+    ref = oracle.prefill(b.q, b.query_start, k, v, b.lens, b.shape.scale)
+    err = float(np.max(np.abs(out.float().cpu().numpy().astype(np.float64) - ref)))
+    say(f"[prefill] out-of-range ids, split={split}: max abs err {err:.3e}")
+    assert np.isfinite(err) and err <= TOL["bf16"], err
