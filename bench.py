@@ -417,7 +417,7 @@ def bench_cfg3(timer, steps, splits):
     stride = (8192 + 1 + steps + sh.block_size) // sh.block_size + 1
     out = torch.empty((b0.B, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
     ws = workspace(b0.B, sh.Hq, stride * sh.block_size, cache.desc, splits)
-    times, times_fused, kvb = [], [], 0.0
+    times, times_fused, times_b2b, kvb = [], [], [], 0.0
     md = StepMetadata(b0.B, stride, depth=4)
     md_host, md_h2d = [], []
     md_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -447,6 +447,9 @@ def bench_cfg3(timer, steps, splits):
         # can be timed on the same state.
         times.append(float(np.median(timer.per_call(run, 5, warmup=1))))
         times_fused.append(float(np.median(timer.per_call(run_fused, 5, warmup=1))))
+        # The same fused step enqueued back to back, as a serving loop runs
+        # ahead of the GPU (each call above also waits for its own launch).
+        times_b2b.append(timer.amortized(run_fused, 10, warmup=1))
         kvb += float(lens.sum().item()) * kv_row_bytes(sh)
         ev = synth.cfg3_churn(step, b0.B, sh)
         for i, pos in enumerate(ev.finished):
@@ -477,6 +480,10 @@ def bench_cfg3(timer, steps, splits):
             "kv_GBps": round(kvb / t / 1e9, 1),
             "seq_steps_per_s": round(b0.B * steps / t, 1),
             "pct_of_hbm_peak": round(100 * kvb / t / 1e9 / HBM_PEAK_GBS, 2),
+            "ms_per_step_back_to_back": round(1e3 * float(np.sum(times_b2b)) / steps, 4),
+            "kv_GBps_back_to_back": round(kvb / float(np.sum(times_b2b)) / 1e9, 1),
+            "pct_of_hbm_peak_back_to_back": round(
+                100 * kvb / float(np.sum(times_b2b)) / 1e9 / HBM_PEAK_GBS, 2),
             "metadata": {"bytes_per_step": 4 * b0.B * (stride + 2),
                          "host_bookkeeping_us": round(1e6 * float(np.median(md_host)), 2),
                          "h2d_us": round(1e6 * float(np.median(md_h2d)), 2),
