@@ -33,12 +33,19 @@ int launch_forked(void *stream, const std::function<int(void *)> &on_main,
     Side &sd = side[dev];
     if (!made[dev]) {
         const unsigned ef = hipEventDisableTiming;
-        if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&sd.fork, ef)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&sd.join, ef)) != hipSuccess) {
+        Side n = {};
+        if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&n.fork, ef)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&n.join, ef)) != hipSuccess) {
+            // Release whatever was made, so a later call starts afresh.
+            if (n.fork)
+                (void)hipEventDestroy(n.fork);
+            if (n.s)
+                (void)hipStreamDestroy(n.s);
             (void)hipGetLastError();
             return fail(PKV_EHIP, "side stream on device %d: %s", dev, hipGetErrorString(e));
         }
+        sd = n;
         made[dev] = true;
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
