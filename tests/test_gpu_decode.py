@@ -182,6 +182,27 @@ def test_empty_context_gives_zeros():
     assert max_err(out[1:], ref) <= TOL["bf16"]
 
 
+def test_lengths_clamped_to_max_context_len():
+    # A device length above max_context_len is clamped to it, a negative one
+    # to 0 (empty context: zeros); the other sequences are unaffected.  The
+    # longest sequence is the one raised past the bound, so that the clamp
+    # lands on its true length.
+    b = synth.cfg2(B=6)
+    cache, q, tab, lens, mx = decode_state(b)
+    i = int(np.argmax(b.lens))
+    j = (i + 2) % b.B
+    assert int(b.lens[i]) == mx
+    lens[i] = mx + 37
+    lens[j] = -5
+    out = run_decode(cache, q, tab, lens, mx, b.shape.scale)
+    assert torch.count_nonzero(out[j]) == 0
+    keep = [s for s in range(b.B) if s != j]
+    ref = oracle.decode(b.q, b.k, b.v, b.lens, b.shape.scale)
+    err = max_err(out[keep], ref[keep])
+    say(f"[decode] clamped lengths: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_bf16_output_rounding():
     b = synth.cfg2(B=4)
     cache, q, tab, lens, mx = decode_state(b)
