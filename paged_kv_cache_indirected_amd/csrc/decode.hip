@@ -80,7 +80,6 @@ constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data forma
 // policy (sc0 or sc1 alone change nothing).
 constexpr int kTilePolicy = 2;
 constexpr int kIdChunk = 2 * kThreads; // block-table entries staged in LDS at a time
-constexpr int kDefer = 64;            // fused-append rows a workgroup writes at its end
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -422,7 +421,6 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     __shared__ int32_t lds_slot[kDecodeMaxSeqs];
     __shared__ __attribute__((aligned(16))) uint4 lds_q[G * LPT];
     __shared__ __attribute__((aligned(16))) uint4 lds_new[2][LPT];   // fused append: K, V row
-    __shared__ int32_t lds_defer[kDefer];     // fused append: sequences whose rows are written at the end
     __shared__ int32_t lds_ids[kIdChunk];
     __shared__ int32_t lds_wsum[NW];
     __shared__ float lds_o[NW][G * OSTR];
@@ -526,7 +524,6 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
     const uint32_t voff = DT == PKV_F32 ? (uint32_t)((g4 * D + n) * 16)
                                         : (uint32_t)((g4 * D + 2 * n) * 8);
 
-    int ndefer = 0;                    // deferred fused-append rows (uniform)
     int64_t x = start;
     while (x < end) {
         while (lds_pref[b + 1] <= x)
@@ -543,12 +540,10 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         // K/V rows of this KV head and their slot: all loads are issued
         // before any is waited for.  The workgroup holding the sequence's
         // last block keeps the new rows in LDS, so that the attention reads
-        // position L-1 from there rather than from the cache, and writes
-        // them to their slot after its last piece: no other workgroup of the
-        // launch reads that block, and stores issued mid-stream would hold
-        // up the tile loads (one in-order counter covers loads and stores;
-        // a lone row's stores are partial cache-line writes).  Beyond
-        // kDefer rows a workgroup writes them at once.
+        // position L-1 from there rather than from the cache; the merge
+        // pass writes them to their slot (no workgroup of this pass reads
+        // the cache at that slot, and stores here would share the in-order
+        // counter with the tile loads or hold the pass's end).
         const int n0 = j1 - j0 < kIdChunk ? j1 - j0 : kIdChunk;
         const bool last_piece = a.k_new && j1 == nblk;
         int32_t nslot = -1;
@@ -574,18 +569,10 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
                 lds_ids[tid] = id0;
             if (tid + kThreads < n0)
                 lds_ids[tid + kThreads] = id1;
-            if ((unsigned)nslot < (unsigned)(a.num_blocks * BS) && tid < 2 * LPT) {
+            if ((unsigned)nslot < (unsigned)(a.num_blocks * BS) && tid < 2 * LPT)
                 lds_new[tid / LPT][tid % LPT] = nv;
-                if (ndefer >= kDefer)
-                    store_new_chunk(a, nslot, g, tid / LPT, tid % LPT, nv);
-            }
         }
         const bool fresh = (unsigned)nslot < (unsigned)(a.num_blocks * BS);
-        if (fresh && ndefer < kDefer) {
-            if (tid == 0)
-                lds_defer[ndefer] = b;
-            ++ndefer;
-        }
         lds_barrier();
 
         // This lane's B operand of S = K Q^T: chunk 4 kk + g4 of query head
@@ -784,18 +771,6 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         x = sb + j1;
         ++b;
     }
-
-    // The deferred fused-append rows: 2 * LPT chunk stores per sequence
-    // (its K and V row of this KV head), the rows reloaded from k_new/v_new.
-    // lds_defer was written before the last piece's barriers.
-    for (int i = tid; i < ndefer * 2 * LPT; i += kThreads) {
-        const int k = i / (2 * LPT), u = i % (2 * LPT);
-        const int bd = lds_defer[k];
-        const int nslot = lds_slot[bd];
-        const uint4 row = static_cast<const uint4 *>(u < LPT ? a.k_new : a.v_new)
-            [((int64_t)bd * a.Hkv + g) * LPT + u % LPT];
-        store_new_chunk(a, nslot, g, u / LPT, u % LPT, row);
-    }
 }
 
 // Log-sum-exp merge of the pieces of every (sequence, query head) cut
@@ -872,22 +847,23 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(Args a)
     const int64_t Ct = (int64_t)a.ws_pref[a.B] + (int64_t)a.piece_cost * a.B;
     const int sb = a.ws_pref[b], se = a.ws_pref[b + 1];
     const int64_t obase = ((int64_t)b * a.Hq + (int64_t)g * G) * D;   // head g*G, dim 0
+    // The fused append: sequence b's new K and V rows of KV head g go to
+    // their slot here, after the split pass (which read them from k_new /
+    // v_new, not from the cache).
+    if (a.k_new && tid < 2 * a.row_chunks) {
+        const int nslot = a.slots[b];
+        if ((unsigned)nslot < (unsigned)(a.num_blocks * a.block_size)) {
+            const int kv = tid / a.row_chunks, i = tid % a.row_chunks;
+            const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
+                [((int64_t)b * a.Hkv + g) * a.row_chunks + i];
+            store_new_chunk(a, nslot, g, kv, i, row);
+        }
+    }
     if (se == sb) {
         for (int i = tid; i < G * D; i += kMergeThreads)
             store_out(a.out, a.out_dtype, obase + i, 0.0f);
         if (a.lse && tid < G)
             a.lse[(int64_t)b * a.Hq + g * G + tid] = -INFINITY;
-        // Fused append of a sequence with no blocks: no split workgroup
-        // visits it, so its new row is written here.
-        if (a.k_new && tid < 2 * a.row_chunks) {
-            const int nslot = a.slots[b];
-            if ((unsigned)nslot < (unsigned)(a.num_blocks * a.block_size)) {
-                const int kv = tid / a.row_chunks, i = tid % a.row_chunks;
-                const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
-                    [((int64_t)b * a.Hkv + g) * a.row_chunks + i];
-                store_new_chunk(a, nslot, g, kv, i, row);
-            }
-        }
         return;
     }
     const int wf = owner(cost_at(sb, b, a.piece_cost), Ct, a.W);
