@@ -253,6 +253,30 @@ __device__ __forceinline__ bool empty_range(int w, int64_t Ct, int W)
     return Ct * w / W == Ct * (w + 1) / W;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2,
+// 4 and 8 (Hillis-Steele within each row of 16), then the totals of the
+// rows below added from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_scan(int v, int lane)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15);
+    const int r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// floor(C * k / W) for 0 <= k <= W < 2^16 and C < 2^31, in 32-bit
+// arithmetic: C = q W + r gives q k + floor(r k / W), r k < 2^32.
+__device__ __forceinline__ uint32_t cut_at(uint32_t C, uint32_t k, uint32_t W)
+{
+    const uint32_t q = C / W, r = C % W;
+    return q * k + (r * k) / W;
+}
+
 // Number of sequences b < B for which pred(b) holds, pred being true on a
 // prefix of b: wave ballots, every wave alone (the result is uniform).
 template <typename P>
@@ -434,9 +458,13 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
 
     // Prefix sums of the per-sequence block counts, and each sequence's
     // clamped length and append slot for the piece set-up (the same in
-    // every workgroup).  Up to 64 sequences every wave computes them alone
-    // and writes the whole tables itself, so it reads them back with no
-    // barrier (the other waves write the same values).
+    // every workgroup); then this workgroup's range [start, end) of the
+    // flattened blocks and its first sequence b.  Up to 64 sequences every
+    // wave computes them alone, in registers, and writes the whole tables
+    // itself, so it reads them back with no barrier (the other waves write
+    // the same values).
+    int T, b;
+    int64_t start, end;
     if (a.B <= 64) {
         // Both loads unconditional (sequence 0 for idle lanes; slots read
         // from the lengths when there is no fused append), so they are in
@@ -450,17 +478,28 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
             lds_len[lane] = Lb;
             lds_slot[lane] = sl;
         }
-        int v = (Lb + BS - 1) / BS;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(v, off);
-            if (lane >= off)
-                v += t;
-        }
+        const int nb = (Lb + BS - 1) / BS;
+        const int v = wave_scan(nb, lane);         // pref[lane + 1]
         if (lane < a.B)
             lds_pref[lane + 1] = v;
         if (lane == 0)
             lds_pref[0] = 0;
+        // The range, from registers: lane s holds pref[s] (ex) and
+        // pref[s + 1] (v) and the cost of its first block (cx).
+        const int ex = v - nb;
+        const uint32_t cx = (uint32_t)(ex + a.piece_cost * lane);
+        T = __builtin_amdgcn_readlane(v, 63);
+        const uint32_t Ct = (uint32_t)T + (uint32_t)a.piece_cost * (uint32_t)a.B;
+        auto at_cost = [&](uint32_t c) -> int64_t {
+            const int lo = __popcll(__ballot(lane < a.B && cx <= c)) - 1;
+            const int x = __builtin_amdgcn_readlane(ex, lo) +
+                          (int)(c - (uint32_t)__builtin_amdgcn_readlane((int)cx, lo));
+            const int p1 = __builtin_amdgcn_readlane(v, lo);
+            return x < p1 ? x : p1;
+        };
+        start = at_cost(cut_at(Ct, wg, a.W));
+        end = at_cost(cut_at(Ct, wg + 1, a.W));
+        b = __popcll(__ballot(lane < a.B && ex <= start)) - 1;
     } else {
         int carry = 0;
         for (int base = 0; base < a.B; base += kThreads) {
@@ -499,22 +538,23 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         if (tid == 0)
             lds_pref[0] = 0;
         lds_barrier();
+        T = lds_pref[a.B];
+        const int64_t Ct = (int64_t)T + (int64_t)a.piece_cost * a.B;
+        start = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * wg / a.W, lane);
+        end = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * (wg + 1) / a.W, lane);
+        // First sequence with blocks in the range: the last b with
+        // pref[b] <= start.
+        b = count_prefix(a.B, lane, [&](int s2) { return lds_pref[s2] <= start; }) - 1;
     }
-    const int T = lds_pref[a.B];
     const int hq0 = g * G;
 
     if (g == 0 && wg == 0)
         for (int i = tid; i <= a.B; i += kThreads)
             a.ws_pref[i] = lds_pref[i];
 
-    const int64_t Ct = (int64_t)T + (int64_t)a.piece_cost * a.B;
-    const int64_t start = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * wg / a.W, lane);
-    const int64_t end = block_at_cost(lds_pref, a.B, a.piece_cost, Ct * (wg + 1) / a.W, lane);
     if (start >= end)
         return;
-
-    // First sequence with blocks in the range: the last b with pref[b] <= start.
-    int b = count_prefix(a.B, lane, [&](int s) { return lds_pref[s] <= start; }) - 1;
+    const int64_t Ct = (int64_t)T + (int64_t)a.piece_cost * a.B;
 
     const int64_t blk_bytes = (int64_t)a.Hkv * TILE;
     const char *kbase = static_cast<const char *>(a.kc) + (int64_t)g * TILE;
