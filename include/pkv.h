@@ -22,6 +22,24 @@
  *     block_table_stride * block_size.
  *   - Return value: PKV_OK (0) or a negative PKV_E* code; pkv_last_error()
  *     then holds a message for the calling thread.
+ *   - Debug build (libpkv_debug.so, built from the same sources with
+ *     PKV_DEBUG defined; same symbols, same results): every call that
+ *     enqueues device work also synchronises `stream` before it returns and
+ *     then reports what the kernels found.  PKV_EHIP if the stream's work
+ *     failed; PKV_EINVAL, naming each violation, if a kernel met a block id
+ *     outside [0, num_blocks), a decode context length outside
+ *     [0, min(block_table_stride * block_size, max_context_len)], a prefill
+ *     context length outside [its chunk's length, block_table_stride *
+ *     block_size], an append slot at or beyond num_blocks * block_size, or a
+ *     copy id at or beyond its cache's block count; then, on the id lists
+ *     read back to the host, if two rows map to one append slot, two copied
+ *     pairs share a destination block, or an in-place copy (same caches)
+ *     has a block that is both a source and a destination.  Negative slots
+ *     and copy ids are padding there too and are not reported.  The check
+ *     reads and clears flag words of the current GPU that all calls share,
+ *     so debug calls must not overlap (one thread, one stream at a time),
+ *     and they cannot be captured into a graph.  The release build
+ *     (libpkv.so) does none of this.
  *   - Element types: q, k, v and the caches share one dtype (PKV_F32 or
  *     PKV_BF16); index arrays are int32.
  *

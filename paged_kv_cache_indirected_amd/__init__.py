@@ -19,7 +19,12 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_DEBUG=1 selects the debug build of the same library: every call that
+# enqueues device work synchronises and returns PKV_EINVAL when a kernel found
+# a device precondition violated (block id, context length, slot), PKV_EHIP
+# on a device error.
+DEBUG = os.environ.get("PKV_DEBUG", "") == "1"
+LIB_PATH = os.path.join(_HERE, "libpkv_debug.so" if DEBUG else "libpkv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

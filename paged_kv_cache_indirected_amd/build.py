@@ -3,7 +3,11 @@
     python -m paged_kv_cache_indirected_amd.build
 
 Host translation units are compiled by g++, HIP ones by hipcc for gfx950
-only, then linked with hipcc into the package directory.
+only, then linked with hipcc into the package directory.  The same sources
+are built a second time with PKV_DEBUG defined into libpkv_debug.so: every
+call that enqueues device work then synchronises and reports the device
+preconditions the kernels found violated (the binding loads it when the
+environment sets PKV_DEBUG=1).
 """
 from __future__ import annotations
 
@@ -18,11 +22,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
+DEBUG_LIB = os.path.join(PKG, "libpkv_debug.so")
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")   # measurement probes, loaded by the benchmark only
 OBJ = os.path.join(ROOT, "_build", "pkv")
+OBJ_DEBUG = os.path.join(ROOT, "_build", "pkv_debug")
 
 HOST_SRC = ["errors.cpp", "pool.cpp", "sched.cpp", "api.cpp"]
-HIP_SRC = ["append.hip", "copy.hip", "decode.hip", "prefill.hip", "side_stream.hip"]
+HIP_SRC = ["append.hip", "copy.hip", "debug.hip", "decode.hip", "prefill.hip", "side_stream.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 vector ops are switched off for all device code.
@@ -48,24 +54,28 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
+    os.makedirs(OBJ_DEBUG, exist_ok=True)
     hipcc = _hipcc()
     jobs = []
-    for s in HOST_SRC:
-        jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, s), "-o",
-                     os.path.join(OBJ, s + ".o")])
-    for s in HIP_SRC:
-        jobs.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, s), "-o",
-                     os.path.join(OBJ, s + ".o")])
+    for obj, extra in ((OBJ, []), (OBJ_DEBUG, ["-DPKV_DEBUG"])):
+        for s in HOST_SRC:
+            jobs.append(["g++", *HOST_FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o",
+                         os.path.join(obj, s + ".o")])
+        for s in HIP_SRC:
+            jobs.append([hipcc, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o",
+                         os.path.join(obj, s + ".o")])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for r in ex.map(_run, jobs):
             if verbose and (r.stdout or r.stderr):
                 print(r.stdout, r.stderr, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    objs = [os.path.join(OBJ, s + ".o") for s in HOST_SRC + HIP_SRC]
-    # -z defs: a symbol left undefined (e.g. a kernel whose host stub was not
-    # emitted) fails the build instead of the library's first load.
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    for obj, lib in ((OBJ, LIB), (OBJ_DEBUG, DEBUG_LIB)):
+        tmp = lib + ".tmp"
+        objs = [os.path.join(obj, s + ".o") for s in HOST_SRC + HIP_SRC]
+        # -z defs: a symbol left undefined (e.g. a kernel whose host stub was
+        # not emitted) fails the build instead of the library's first load.
+        _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o",
+              tmp])
+        os.replace(tmp, lib)
     tmp = PROBE_LIB + ".tmp"
     _run([hipcc, *HIP_FLAGS, "-shared", os.path.join(CSRC, "probe.hip"), "-o", tmp])
     os.replace(tmp, PROBE_LIB)

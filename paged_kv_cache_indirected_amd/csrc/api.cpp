@@ -160,7 +160,9 @@ extern "C" int pkv_append(const void *k, const void *v, const int32_t *slot_mapp
         return fail(PKV_EINVAL, "%s: slot_mapping is NULL", who);
     pkv::AppendLaunch a{k, v, slot_mapping, num_tokens, k_cache, v_cache, c->num_blocks,
                         c->num_kv_heads, c->block_size, c->head_dim, elem_size(c->dtype), stream};
-    return pkv::launch_append(a);
+    rc = PKV_FINISH(pkv::launch_append(a), stream, who);
+    return PKV_CHECK_SLOTS(rc, slot_mapping, num_tokens,
+                           (int64_t)c->num_blocks * c->block_size, stream, who);
 }
 
 extern "C" int pkv_copy_blocks(const void *src_k, const void *src_v, const pkv_cache_desc *src_c,
@@ -192,7 +194,9 @@ extern "C" int pkv_copy_blocks(const void *src_k, const void *src_v, const pkv_c
                     (long long)block_bytes);
     pkv::CopyLaunch a{src_k, src_v, src_c->num_blocks, dst_k, dst_v, dst_c->num_blocks,
                       src_ids, dst_ids, n, block_bytes, stream};
-    return pkv::launch_copy_blocks(a);
+    rc = PKV_FINISH(pkv::launch_copy_blocks(a), stream, who);
+    return PKV_CHECK_COPY_IDS(rc, src_ids, dst_ids, n, src_c->num_blocks, dst_c->num_blocks,
+                              src_k == dst_k || src_v == dst_v, stream, who);
 }
 
 extern "C" int32_t pkv_decode_num_splits(int32_t num_seqs, int32_t num_q_heads,
@@ -342,10 +346,11 @@ extern "C" int pkv_decode(const void *q, const void *k_cache, const void *v_cach
                           const pkv_cache_desc *c, void *stream)
 {
     pkv::clear_error();
-    return decode_call("pkv_decode", q, k_cache, v_cache, block_tables, block_table_stride,
-                       context_lens, num_seqs, num_q_heads, max_context_len, scale, out, out_dtype,
-                       num_splits, workspace, workspace_bytes, c, stream, nullptr, nullptr,
-                       nullptr);
+    const int rc = decode_call("pkv_decode", q, k_cache, v_cache, block_tables,
+                               block_table_stride, context_lens, num_seqs, num_q_heads,
+                               max_context_len, scale, out, out_dtype, num_splits, workspace,
+                               workspace_bytes, c, stream, nullptr, nullptr, nullptr);
+    return PKV_FINISH(rc, stream, "pkv_decode");
 }
 
 extern "C" int pkv_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
@@ -382,9 +387,10 @@ extern "C" int pkv_decode_noalloc(const void *q, const void *k_cache, const void
     void *ws = nullptr;
     if ((rc = pkv::decode_noalloc_scratch(&ws)))
         return rc;
-    return decode_call(who, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
-                       num_seqs, num_q_heads, max_context_len, scale, out, out_dtype, num_splits,
-                       ws, PKV_DECODE_NOALLOC_SCRATCH_BYTES, c, stream, nullptr, nullptr, nullptr);
+    rc = decode_call(who, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                     num_seqs, num_q_heads, max_context_len, scale, out, out_dtype, num_splits,
+                     ws, PKV_DECODE_NOALLOC_SCRATCH_BYTES, c, stream, nullptr, nullptr, nullptr);
+    return PKV_FINISH(rc, stream, who);
 }
 
 extern "C" int pkv_append_decode(const void *k_new, const void *v_new,
@@ -399,10 +405,13 @@ extern "C" int pkv_append_decode(const void *k_new, const void *v_new,
     pkv::clear_error();
     if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
         return fail(PKV_EINVAL, "pkv_append_decode: k_new, v_new or slot_mapping is NULL");
-    return decode_call("pkv_append_decode", q, k_cache, v_cache, block_tables, block_table_stride,
-                       context_lens, num_seqs, num_q_heads, max_context_len, scale, out, out_dtype,
-                       num_splits, workspace, workspace_bytes, c, stream, k_new, v_new,
-                       slot_mapping);
+    const int rc = decode_call("pkv_append_decode", q, k_cache, v_cache, block_tables,
+                               block_table_stride, context_lens, num_seqs, num_q_heads,
+                               max_context_len, scale, out, out_dtype, num_splits, workspace,
+                               workspace_bytes, c, stream, k_new, v_new, slot_mapping);
+    return PKV_CHECK_SLOTS(PKV_FINISH(rc, stream, "pkv_append_decode"), slot_mapping, num_seqs,
+                           c ? (int64_t)c->num_blocks * c->block_size : 0, stream,
+                           "pkv_append_decode");
 }
 
 extern "C" size_t pkv_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -495,8 +504,9 @@ extern "C" int pkv_decode_cascade(const void *q, const void *k_cache, const void
     rc = ks > 0 ? pkv::launch_forked(stream, suffixes, prefix) : suffixes(stream);
     if (rc != PKV_OK)
         return rc;
-    return pkv::launch_merge_states(o_all, lse_all, ks + 1, rows, c->head_dim, out, out_dtype,
-                                    stream);
+    return PKV_FINISH(pkv::launch_merge_states(o_all, lse_all, ks + 1, rows, c->head_dim, out,
+                                               out_dtype, stream),
+                      stream, who);
 }
 
 extern "C" size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -557,7 +567,7 @@ extern "C" int pkv_prefill_chunk(const void *q, const int32_t *query_start_loc, 
                workspace_bytes)
         --ks;
     if (ks <= 1)
-        return pkv::launch_prefill(p);
+        return PKV_FINISH(pkv::launch_prefill(p), stream, who);
     if ((rc = check_ptr(workspace, "workspace", who)))
         return rc;
     const PrefillWs lay = prefill_layout(num_seqs, num_q_heads, max_query_len, c->head_dim, ks);
@@ -570,6 +580,7 @@ extern "C" int pkv_prefill_chunk(const void *q, const int32_t *query_start_loc, 
     p.split_rows = lay.rows;
     if ((rc = pkv::launch_prefill(p)))
         return rc;
-    return pkv::launch_merge_states(so, sl, ks, lay.rows, c->head_dim, out, out_dtype, stream,
-                                    query_start_loc + num_seqs, num_q_heads);
+    return PKV_FINISH(pkv::launch_merge_states(so, sl, ks, lay.rows, c->head_dim, out, out_dtype,
+                                               stream, query_start_loc + num_seqs, num_q_heads),
+                      stream, who);
 }

@@ -21,6 +21,14 @@
 
 #include "pkv_internal.h"
 
+#ifdef PKV_DEBUG
+// Device preconditions found violated by this module's kernels (kDbg* bits).
+static __device__ uint32_t dbg_word;
+#define PKV_DBG_NOTE(bit) atomicOr(&dbg_word, (bit))
+#else
+#define PKV_DBG_NOTE(bit) ((void)0)
+#endif
+
 namespace pkv {
 namespace {
 
@@ -53,6 +61,8 @@ __global__ __launch_bounds__(kThreads) void k_append(const char *__restrict__ k,
     const int nrow = T - t0 < 4 ? T - t0 : 4;
     // Slots of the group's rows (lanes 0 .. 3), then wave-uniform copies.
     const int sl = lane < nrow ? slots[t0 + lane] : -1;
+    if (sl >= cap_slots)                                 // (negative: padding)
+        PKV_DBG_NOTE(kDbgSlot);
     int s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -172,5 +182,18 @@ int launch_append(const AppendLaunch &a)
         return fail(PKV_EHIP, "pkv_append: launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
+
+#ifdef PKV_DEBUG
+uint32_t append_debug_take()
+{
+    uint32_t v = 0, z = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(dbg_word), sizeof v) != hipSuccess ||
+        hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &z, sizeof z) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return v;
+}
+#endif
 
 }  // namespace pkv

@@ -19,6 +19,14 @@
 
 #include "pkv_internal.h"
 
+#ifdef PKV_DEBUG
+// Device preconditions found violated by this module's kernels (kDbg* bits).
+static __device__ uint32_t dbg_word;
+#define PKV_DBG_NOTE(bit) atomicOr(&dbg_word, (bit))
+#else
+#define PKV_DBG_NOTE(bit) ((void)0)
+#endif
+
 namespace pkv {
 namespace {
 
@@ -39,8 +47,11 @@ __global__ __launch_bounds__(kThreads) void k_copy_blocks(
     const int32_t tensor = (x / pieces) & 1;
     const int32_t piece = x % pieces;
     const int32_t s = src_ids[pair], d = dst_ids[pair];
-    if (s < 0 || s >= src_nb || d < 0 || d >= dst_nb)   // outside a cache: pair skipped
+    if (s < 0 || s >= src_nb || d < 0 || d >= dst_nb) {   // outside a cache: pair skipped
+        if (threadIdx.x == 0 && (s >= src_nb || d >= dst_nb))   // (negative: padding)
+            PKV_DBG_NOTE(kDbgCopyId);
         return;
+    }
     const char *src = (tensor ? sv : sk) + (size_t)s * block_bytes;
     char *dst = (tensor ? dv : dk) + (size_t)d * block_bytes;
     const int32_t base = piece * kPiece + threadIdx.x * 16;
@@ -80,5 +91,18 @@ int launch_copy_blocks(const CopyLaunch &a)
         return fail(PKV_EHIP, "pkv_copy_blocks: launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
+
+#ifdef PKV_DEBUG
+uint32_t copy_debug_take()
+{
+    uint32_t v = 0, z = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(dbg_word), sizeof v) != hipSuccess ||
+        hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &z, sizeof z) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return v;
+}
+#endif
 
 }  // namespace pkv

@@ -60,6 +60,14 @@
 
 #include "pkv_internal.h"
 
+#ifdef PKV_DEBUG
+// Device preconditions found violated by this module's kernels (kDbg* bits).
+static __device__ uint32_t dbg_word;
+#define PKV_DBG_NOTE(bit) atomicOr(&dbg_word, (bit))
+#else
+#define PKV_DBG_NOTE(bit) ((void)0)
+#endif
+
 // Split partials of pkv_decode_noalloc (callers that cannot allocate device
 // memory).  Each GPU the library runs on holds its own copy until the
 // process ends; in host code the name is only a handle for the symbol
@@ -473,6 +481,8 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         const int bi = lane < a.B ? lane : 0;
         const int rl = a.lens[bi], sr = sp[bi];
         const int Lb = lane < a.B ? clamp_raw_len<BS>(a, rl) : 0;
+        if (lane < a.B && Lb != rl)
+            PKV_DBG_NOTE(kDbgLength);
         const int sl = a.k_new ? sr : -1;
         if (lane < a.B) {
             lds_len[lane] = Lb;
@@ -508,6 +518,8 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
             const int bi = b < a.B ? b : 0;
             const int rl = a.lens[bi], sr = sp[bi];
             const int Lb = b < a.B ? clamp_raw_len<BS>(a, rl) : 0;
+            if (b < a.B && Lb != rl)
+                PKV_DBG_NOTE(kDbgLength);
             const int sl = a.k_new ? sr : -1;
             if (b < a.B) {
                 lds_len[b] = Lb;
@@ -605,6 +617,9 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
             }
             if (tid < G * LPT)
                 lds_q[tid] = qv;
+            if ((tid < n0 && (unsigned)id0 >= (unsigned)a.num_blocks) ||
+                (tid + kThreads < n0 && (unsigned)id1 >= (unsigned)a.num_blocks))
+                PKV_DBG_NOTE(kDbgBlockId);
             if (tid < n0)
                 lds_ids[tid] = id0;
             if (tid + kThreads < n0)
@@ -714,8 +729,12 @@ __global__ __launch_bounds__(kThreads, (DT == PKV_F32 && D == 128) ? 1 : 2) void
         for (; c0 < j1; c0 += kIdChunk) {
           const int c1 = j1 - c0 < kIdChunk ? j1 : c0 + kIdChunk;
           if (c0 != j0) {                  // the first chunk came with the q rows
-              for (int i = tid; i < c1 - c0; i += kThreads)
-                  lds_ids[i] = bt[c0 + i];
+              for (int i = tid; i < c1 - c0; i += kThreads) {
+                  const int32_t id = bt[c0 + i];
+                  if ((unsigned)id >= (unsigned)a.num_blocks)
+                      PKV_DBG_NOTE(kDbgBlockId);
+                  lds_ids[i] = id;
+              }
               lds_barrier();
           }
           if (c0 + w < c1) {
@@ -892,6 +911,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(Args a)
     // v_new, not from the cache).
     if (a.k_new && tid < 2 * a.row_chunks) {
         const int nslot = a.slots[b];
+        if (nslot >= a.num_blocks * a.block_size)         // (negative: padding)
+            PKV_DBG_NOTE(kDbgSlot);
         if ((unsigned)nslot < (unsigned)(a.num_blocks * a.block_size)) {
             const int kv = tid / a.row_chunks, i = tid % a.row_chunks;
             const uint4 row = static_cast<const uint4 *>(kv ? a.v_new : a.k_new)
@@ -1152,5 +1173,18 @@ int launch_merge_states(const float *o, const float *lse, int32_t k, int64_t row
         return fail(PKV_EHIP, "state merge launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
+
+#ifdef PKV_DEBUG
+uint32_t decode_debug_take()
+{
+    uint32_t v = 0, z = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(dbg_word), sizeof v) != hipSuccess ||
+        hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &z, sizeof z) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return v;
+}
+#endif
 
 }  // namespace pkv

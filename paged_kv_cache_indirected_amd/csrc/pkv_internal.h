@@ -9,6 +9,39 @@
 
 namespace pkv {
 
+// Debug builds (PKV_DEBUG, libpkv_debug.so): the kernels record the device
+// preconditions they find violated in a word per kernel module (bits
+// below; the release build handles the same inputs silently: blocks read
+// as zeros, lengths clamped, slots and pairs skipped), and every entry
+// point that enqueued work synchronises its stream and turns a set word
+// into PKV_EINVAL, a device error into PKV_EHIP (debug_finish).
+constexpr uint32_t kDbgBlockId = 1u;   // block id outside the pool
+constexpr uint32_t kDbgLength = 2u;    // context length outside its bound, or a chunk longer
+constexpr uint32_t kDbgSlot = 4u;      // append slot beyond the cache
+constexpr uint32_t kDbgCopyId = 8u;    // block copy id outside its cache
+#ifdef PKV_DEBUG
+// Each returns and clears its module's word on the current device.
+uint32_t append_debug_take();
+uint32_t copy_debug_take();
+uint32_t decode_debug_take();
+uint32_t prefill_debug_take();
+int debug_finish(int rc, void *stream, const char *who);
+// Host-side checks of the distinctness preconditions, on the id lists read
+// back after the call: append slots in [0, cap) distinct; copy destinations
+// of the pairs copied distinct and, in place, none of them also a source.
+int debug_slots(int rc, const int32_t *slots, int64_t n, int64_t cap, void *stream,
+                const char *who);
+int debug_copy_ids(int rc, const int32_t *src_ids, const int32_t *dst_ids, int64_t n,
+                   int64_t src_nb, int64_t dst_nb, bool in_place, void *stream, const char *who);
+#define PKV_FINISH(rc, stream, who) pkv::debug_finish((rc), (stream), (who))
+#define PKV_CHECK_SLOTS(rc, ...) pkv::debug_slots((rc), __VA_ARGS__)
+#define PKV_CHECK_COPY_IDS(rc, ...) pkv::debug_copy_ids((rc), __VA_ARGS__)
+#else
+#define PKV_FINISH(rc, stream, who) (rc)
+#define PKV_CHECK_SLOTS(rc, ...) (rc)
+#define PKV_CHECK_COPY_IDS(rc, ...) (rc)
+#endif
+
 // Record a failure for pkv_last_error() and return `code`.
 int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();

@@ -42,6 +42,14 @@
 
 #include "pkv_internal.h"
 
+#ifdef PKV_DEBUG
+// Device preconditions found violated by this module's kernels (kDbg* bits).
+static __device__ uint32_t dbg_word;
+#define PKV_DBG_NOTE(bit) atomicOr(&dbg_word, (bit))
+#else
+#define PKV_DBG_NOTE(bit) ((void)0)
+#endif
+
 namespace pkv {
 namespace {
 
@@ -178,6 +186,8 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
     const int C = a.syn_rows > 0 ? a.syn_rows : a.qsl[s + 1] - q0;
     int L = seq_len<BS>(a, s);
     const int cap = a.stride * BS;
+    if (a.syn_rows == 0 && (L < 0 || L > cap || L < C))
+        PKV_DBG_NOTE(kDbgLength);
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int p0 = L - C;                            // keys before the chunk
     const int tok0 = qt * TQ;
@@ -255,6 +265,8 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int jb = chunk * IDS + tid + k * kThreads;
+            if (jb < nblk && (unsigned)idv[k] >= (unsigned)a.num_blocks)
+                PKV_DBG_NOTE(kDbgBlockId);
             lds_ids[tid + k * kThreads] = jb < nblk ? idv[k] : -1;
         }
     };
@@ -625,5 +637,18 @@ int launch_prefill(const PrefillLaunch &p)
         return fail(PKV_EHIP, "pkv_prefill_chunk: launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
+
+#ifdef PKV_DEBUG
+uint32_t prefill_debug_take()
+{
+    uint32_t v = 0, z = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(dbg_word), sizeof v) != hipSuccess ||
+        hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &z, sizeof z) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return v;
+}
+#endif
 
 }  // namespace pkv

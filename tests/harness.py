@@ -54,6 +54,27 @@ def decode_state(batch: synth.DecodeBatch, pool_seed=None, poison=None, share_pr
     return cache, q, tables, lens, max_len
 
 
+def step_state(batch, pool_seed=None):
+    """Cache holding every row but each sequence's last; the step's slots
+    from the pool; the last rows as device tensors.  Returns (cache, slots,
+    k_new, v_new, q, tables, lens, max_len)."""
+    sh = batch.shape
+    st = batch.seq_start()
+    ids = list(range(batch.B))
+    cache = PagedCache(batch.pool_blocks, sh.Hkv, sh.block_size, sh.D, DT[sh.dtype],
+                       pool_seed=batch.pool_seed if pool_seed is None else pool_seed)
+    cache.add_sequences(ids, batch.lens - 1,
+                        np.concatenate([batch.k[st[b]:st[b + 1] - 1] for b in ids]),
+                        np.concatenate([batch.v[st[b]:st[b + 1] - 1] for b in ids]))
+    slots = cache.seqs.append_batch(ids)
+    tables, lens, mx = cache.tables(ids)
+    last = st[1:] - 1
+    return (cache, torch.from_numpy(slots).to(cache.device),
+            to_device_rows(batch.k[last], DT[sh.dtype], cache.device),
+            to_device_rows(batch.v[last], DT[sh.dtype], cache.device),
+            to_device_rows(batch.q, DT[sh.dtype], cache.device), tables, lens, mx)
+
+
 def run_decode(cache: PagedCache, q, tables, lens, max_len, scale, out_dtype=torch.float32,
                num_splits=0):
     B, Hq, D = q.shape

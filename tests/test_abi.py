@@ -29,6 +29,17 @@ def test_every_declared_symbol_is_exported():
     assert not missing, missing
 
 
+def test_debug_library_exports_every_declared_symbol():
+    """libpkv_debug.so (PKV_DEBUG: synchronising, device-checked calls) is a
+    drop-in for libpkv.so: same symbols, same ABI version."""
+    path = os.path.join(os.path.dirname(pkv.LIB_PATH), "libpkv_debug.so")
+    lib = ctypes.CDLL(path)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    lib.pkv_abi_version.restype = ctypes.c_int
+    assert lib.pkv_abi_version() == pkv.abi_version()
+
+
 def test_abi_version_and_strerror():
     assert pkv.abi_version() == 2
     for code in (pkv.OK, pkv.EINVAL, pkv.EUNSUPPORTED, pkv.ENOBLOCKS, pkv.ESTATE, pkv.EHIP):

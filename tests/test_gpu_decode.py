@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synth
-from harness import TOL, decode_state, max_err, run_decode, sample_pairs, say
+from harness import TOL, decode_state, max_err, run_decode, sample_pairs, say, step_state
 
 pytestmark = pytest.mark.gpu
 
@@ -254,28 +254,6 @@ def test_workspace_reused_across_calls():
             assert max_err(out, ref) <= TOL["bf16"], ns
 
 
-def _step_state(batch, pool_seed=None):
-    """Cache holding every row but each sequence's last; the step's slots
-    from the pool; the last rows as device tensors."""
-    from paged_kv_cache_indirected_amd.paged import PagedCache, to_device_rows
-    from harness import DT
-    sh = batch.shape
-    st = batch.seq_start()
-    ids = list(range(batch.B))
-    cache = PagedCache(batch.pool_blocks, sh.Hkv, sh.block_size, sh.D, DT[sh.dtype],
-                       pool_seed=batch.pool_seed if pool_seed is None else pool_seed)
-    cache.add_sequences(ids, batch.lens - 1,
-                        np.concatenate([batch.k[st[b]:st[b + 1] - 1] for b in ids]),
-                        np.concatenate([batch.v[st[b]:st[b + 1] - 1] for b in ids]))
-    slots = cache.seqs.append_batch(ids)
-    tables, lens, mx = cache.tables(ids)
-    last = st[1:] - 1
-    return (cache, torch.from_numpy(slots).to("cuda"),
-            to_device_rows(batch.k[last], DT[sh.dtype], "cuda"),
-            to_device_rows(batch.v[last], DT[sh.dtype], "cuda"),
-            to_device_rows(batch.q, DT[sh.dtype], "cuda"), tables, lens, mx)
-
-
 @pytest.mark.parametrize("name", ["cfg1", "cfg2", "ragged-bs32-f32", "many-short"])
 def test_append_decode_equals_append_then_decode_bitwise(name):
     import paged_kv_cache_indirected_amd as pkv
@@ -296,7 +274,7 @@ def test_append_decode_equals_append_then_decode_bitwise(name):
         b = synth.custom_decode(15, [1, 2, 31, 32, 33, 100], Hq=8, Hkv=2, D=128, dtype="f32",
                                 block_size=32)
     say(f"[append_decode] {name}")
-    cache, slots, kn, vn, q, tab, lens, mx = _step_state(b)
+    cache, slots, kn, vn, q, tab, lens, mx = step_state(b)
     kc0, vc0 = cache.k_cache.clone(), cache.v_cache.clone()
     B, Hq, D = q.shape
     for ns in splits:
@@ -330,7 +308,7 @@ def test_append_decode_skipped_slots_and_empty_sequences():
     import paged_kv_cache_indirected_amd as pkv
     b = synth.custom_decode(16, [40, 1, 17, 300], Hq=16, Hkv=2, D=128, dtype="bf16",
                             block_size=16)
-    cache, slots, kn, vn, q, tab, lens, mx = _step_state(b)
+    cache, slots, kn, vn, q, tab, lens, mx = step_state(b)
     pkv.append(kn[:1], vn[:1], slots[:1], cache.k_cache, cache.v_cache, cache.desc)
     slots_f = slots.clone()
     slots_f[0] = -1
