@@ -65,6 +65,29 @@ def test_shape_sweep_ragged(D, bs, G):
     _check(b, label="sweep")
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_empty_chunk_and_max_query_len_above_every_chunk(split):
+    # A sequence with no chunk rows between two that have some, and a
+    # max_query_len (and so a grid and a split workspace) larger than any
+    # chunk: the rows that exist match the oracle, nothing else is written.
+    b = synth.custom_prefill(318, prior=[10, 3000, 0], chunk=[20, 0, 5], Hq=16, Hkv=2, D=128,
+                             block_size=16)
+    say(f"[prefill] empty chunk, max_query_len 200, split={split}")
+    cache, q, qs, tab, lens, mx = prefill_state(b)
+    T, Hq, D = q.shape
+    out = torch.full((T + 3, Hq, D), 7.0, dtype=torch.float32, device=q.device)
+    ws = None
+    if split:
+        n = pkv.prefill_workspace_bytes(3, Hq, 200, cache.desc)
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    pkv.prefill_chunk(q, qs, cache.k_cache, cache.v_cache, tab, lens, b.shape.scale, out[:T],
+                      cache.desc, 200, mx, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(b.q, b.query_start, b.k, b.v, b.lens, b.shape.scale)
+    assert max_err(out[:T], ref) <= TOL["bf16"]
+    assert torch.all(out[T:] == 7.0)
+
+
 def test_first_chunk_of_a_prompt_p0_zero():
     b = synth.custom_prefill(310, prior=[0, 0], chunk=[512, 3], Hq=64, Hkv=8, D=128,
                              block_size=16)
