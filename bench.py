@@ -1035,6 +1035,36 @@ def probe_copy(nbytes=1 << 30, reps=3):
     print(json.dumps({"probe_copy_bytes": nbytes, "reps": reps}))
 
 
+def probe_coissue(iters=20000, reps=3):
+    """Matrix-core work beside vector work on one SIMD (pkv_probe_coissue):
+    256 workgroups of 8 waves, waves w and w + 4 on one SIMD; each mode
+    timed with HIP events on the launch stream, reps times, alternating."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_indirected_amd", "libpkv_probe.so"))
+    P = ctypes.c_void_p
+    lib.pkv_probe_coissue.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
+    grid = 256
+    out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    names = ["mfma_waves_beside_fma_waves", "mfma_waves_alone", "fma_waves_alone",
+             "one_wave_interleaved_1_mfma_3_fma"]
+    times = {n: [] for n in names}
+    for _ in range(reps):
+        for mode, n in enumerate(names):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            rc = lib.pkv_probe_coissue(out.data_ptr(), iters, mode, grid, st.cuda_stream)
+            e1.record(st)
+            e1.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"pkv_probe_coissue: {rc}")
+            times[n].append(e0.elapsed_time(e1))
+    print(json.dumps({"probe": "coissue", "iters": iters, "workgroups": grid,
+                      "per_iteration": "8 v_mfma_f32_16x16x32_bf16 per MFMA wave, 24 fp32 FMA "
+                                       "per FMA wave",
+                      "ms": {n: [round(t, 3) for t in v] for n, v in times.items()}}))
+
+
 def _pmc_per_dispatch(csv_path, name_part, counter):
     import csv
     vals = {}
@@ -1178,6 +1208,8 @@ def main():
                                        "prefix_cache_ttft", "step_scheduler",
                                        "decode_batch_sweep"],
                     help="run one secondary workload alone (for profiling) and print its JSON")
+    ap.add_argument("--probe-coissue", action="store_true",
+                    help="time matrix-core work beside vector work on one SIMD and exit")
     ap.add_argument("--probe-copy", action="store_true",
                     help="run only the copy probe (for hardware-counter scaling)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -1204,6 +1236,9 @@ def main():
         b = synth.cfg2()
         pmc_summary(*args.pmc_summary, PMC_FILE, 1 << 30,
                     float(b.lens.sum()) * kv_row_bytes(b.shape))
+        return
+    if args.probe_coissue:
+        probe_coissue()
         return
     if args.probe_copy:
         probe_copy()

@@ -13,6 +13,9 @@
 //   pkv_probe_copy         copy n 16-byte chunks: a kernel of known traffic
 //                          (n * 16 bytes read, n * 16 written) against which
 //                          hardware byte counters are scaled.
+//   pkv_probe_coissue      matrix-core work beside vector work on one SIMD:
+//                          how much of one instruction stream hides under
+//                          the other (the prefill's softmax beside its MFMAs).
 // Each reader folds what it loads into an XOR kept in one word per
 // workgroup so that no load can be dropped.  The readers' loads carry the
 // non-temporal hint, as the decode's tile loads do (every byte is read once).
@@ -137,6 +140,67 @@ __global__ __launch_bounds__(kThreads) void k_copy(const uint4 *__restrict__ src
         dst[i] = src[i];
 }
 
+// Waves w and w + 4 of an 8-wave workgroup share a SIMD.  Per iteration an
+// MFMA wave issues 8 independent v_mfma_f32_16x16x32_bf16 and an FMA wave 24
+// independent fp32 FMAs (96 vector cycles against 128 matrix cycles).
+// mode 0: waves 0-3 MFMA, waves 4-7 FMA; 1: the MFMA waves alone; 2: the FMA
+// waves alone; 3: waves 0-3 issue both streams, 1 MFMA then 3 FMAs.  Each
+// thread writes one word of out, so nothing is dropped.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(512, 1) void k_coissue(float *out, int iters, int mode)
+{
+    const int tid = threadIdx.x;
+    const int half = tid >> 8;                       // 0: waves 0-3, 1: waves 4-7
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (float)(tid + i));
+        b[i] = (__bf16)(0.002f * (float)i);
+    }
+    f32x4 c[8];
+    float x[8];
+    for (int j = 0; j < 8; ++j) {
+        c[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        x[j] = 0.5f + 0.01f * (float)(tid + j);
+    }
+    const float m = 0.999f, ad = 0.001f;
+    const bool mfma = half == 0 && mode != 2;
+    const bool fma = (half == 1 && mode != 1 && mode != 3) || (half == 0 && mode == 3);
+    if (mfma && !fma) {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
+    } else if (fma && !mfma) {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[j] = __builtin_fmaf(x[j], m, ad);
+    } else if (mfma && fma) {
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 3; ++r)
+                    x[(j + 3 * r) % 8] = __builtin_fmaf(x[(j + 3 * r) % 8], m, ad);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three vector ops
+            }
+        }
+    }
+    float r = 0.0f;
+    for (int j = 0; j < 8; ++j)
+        r += c[j][0] + c[j][1] + c[j][2] + c[j][3] + x[j];
+    out[(size_t)blockIdx.x * 512 + tid] = r;
+}
+
 int finish()
 {
     return hipGetLastError() == hipSuccess ? 0 : -5;
@@ -173,5 +237,16 @@ extern "C" int pkv_probe_copy(const void *src, void *dst, size_t n16, int grid, 
     hipLaunchKernelGGL(k_copy, dim3(grid), dim3(kThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), static_cast<const uint4 *>(src),
                        static_cast<uint4 *>(dst), n16);
+    return finish();
+}
+
+// out must hold grid * 512 floats.  Return 0, -1 on a bad argument, or -5
+// on a launch error.
+extern "C" int pkv_probe_coissue(void *out, int iters, int mode, int grid, void *stream)
+{
+    if (!out || iters < 0 || mode < 0 || mode > 3 || grid <= 0)
+        return -1;
+    hipLaunchKernelGGL(k_coissue, dim3(grid), dim3(512), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<float *>(out), iters, mode);
     return finish();
 }
