@@ -88,6 +88,20 @@ def test_empty_chunk_and_max_query_len_above_every_chunk(split):
     assert torch.all(out[T:] == 7.0)
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_block_table_longer_than_one_id_list(split):
+    # More than 1024 blocks in a sequence's table: the kernel that restages
+    # block ids in chunks (the pipelined one keeps them in one LDS list).
+    b = synth.custom_prefill(319, prior=[17000, 30], chunk=[40, 9], Hq=16, Hkv=2, D=128,
+                             block_size=16)
+    say(f"[prefill] long table ({int(b.lens.max()) // 16 + 1} blocks), split={split}")
+    cache, q, qs, tab, lens, mx = prefill_state(b)
+    assert tab.shape[1] > 1024
+    out = run_prefill(cache, q, qs, tab, lens, mx, b.shape.scale, 40, split=split)
+    ref = oracle.prefill(b.q, b.query_start, b.k, b.v, b.lens, b.shape.scale)
+    assert max_err(out, ref) <= TOL["bf16"]
+
+
 def test_first_chunk_of_a_prompt_p0_zero():
     b = synth.custom_prefill(310, prior=[0, 0], chunk=[512, 3], Hq=64, Hkv=8, D=128,
                              block_size=16)
