@@ -925,9 +925,8 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
     };
     // P^T operands of k-step s2 (keys 32 s2 ..), hi = p truncated to bf16,
     // lo = bf16(p - hi), from the exponentials in sacc[2 s2], sacc[2 s2 + 1].
-    auto split_p = [&](int s2) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
+    auto split_pc = [&](int s2, int ct) {
+        {
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
@@ -945,6 +944,11 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
             phi[ct][s2] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
             plo[ct][s2] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
         }
+    };
+    auto split_p = [&](int s2) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            split_pc(s2, ct);
     };
     // A tile no row masks, as one branch-free block (after the rarely
     // taken O rescale for the previous tile's max growth) whose order is
@@ -1011,8 +1015,8 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
                     lsum[ct] = __builtin_fmaf(lsum[ct], alpha[ct], sum[ct]);
-            } else if (i == NCT + 11) {
-                split_p(0);              // the first k-step's P operands
+            } else if (i < NCT + 11 + NCT) {
+                split_pc(0, i - (NCT + 11));   // the first k-step's P operands
             }
         };
         // Part A: 2 NDT PV steps (hi of dims tile dt, lo of dt - 1) beside
@@ -1047,7 +1051,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
                 vnext1 = vnext2;
                 fence();
             }
-        for (; slice < NCT + 12; ++slice)   // (head_dim 64: fewer PV steps than slices)
+        for (; slice < NCT + 11 + NCT; ++slice)   // (head_dim 64: fewer PV steps than slices)
             sm_slice(slice);
         // Part B: the next tile's S in 2 NDS steps beside the split of the
         // second k-step and the staging.
@@ -1078,8 +1082,8 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
             }
             kcur[0] = knext[0];
             kcur[1] = knext[1];
-            if (step == 0)
-                split_p(1);
+            if (step < NCT)
+                split_pc(1, step);
             if (step == NDS) {
                 store_k(kt + 2);
                 store_v(kt, std::false_type{});
