@@ -36,11 +36,13 @@
 //   * Grid (Hkv, q-tiles, sequences): the KV head is fastest so all q-tiles
 //     of one (sequence, head) land on one XCD and share its L2; q-tiles run
 //     last-to-first, the longest (most keys) first.
-//   * Two loop forms.  k_prefill_sp (the default, block tables of up to
-//     kIdChunk entries) pipelines consecutive key tiles inside each wave,
-//     so that its MFMAs have vector work beside them; k_prefill (longer
-//     tables, whose block ids it restages in chunks) computes a tile's S,
-//     softmax and PV in turn.
+//   * The loop is software-pipelined inside each wave: the body for key
+//     tile kt runs tile kt - 1's PV product beside tile kt's softmax and
+//     P split, and tile kt + 1's S product beside the staging, in slots
+//     whose order scheduling fences fix, so that the matrix cores have
+//     vector work of the same wave beside them.  One LDS-only barrier per
+//     tile.  Block ids stream through a ring in LDS, so tables of any
+//     length work.
 // Unused slots and keys past the context are staged as zeros and masked; a
 // block id outside the pool is read as zeros without touching memory.
 #include <hip/hip_runtime.h>
@@ -72,7 +74,7 @@ constexpr int NCT = 2;                 // 16-column MFMA tiles per wave
 constexpr int WROWS = 16 * NCT;        // query rows per wave
 constexpr int ROWS = NW * WROWS;       // query rows per workgroup
 constexpr float kLazyMax = 8.0f;       // running-max slack, log2 units
-constexpr int kIdChunk = 1024;         // block ids staged in LDS at a time
+constexpr int kIdChunk = 1024;         // slots of the LDS ring of block ids
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer resource: 32-bit data format, no swizzle
 
 template <int D>
@@ -152,435 +154,13 @@ __device__ __forceinline__ float xsum(float v)
     return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
 }
 
-template <int D, int BS, int G>
-__global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
-{
-    using Sh = PShape<D>;
-    constexpr int TQ = ROWS / G;                     // chunk tokens per workgroup
-    constexpr int NDS = Sh::NDS, NDT = Sh::NDT, CPR = Sh::CPR, VK = Sh::VK;
-    constexpr int KSTR = Sh::KSTR, VPS = Sh::VPS;
-    constexpr int IDS = kIdChunk;                    // block ids staged per chunk
-    constexpr int CT = IDS * BS / KT;                // key tiles per id chunk
-
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][Sh::KBUF];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][Sh::VBUF];
-    __shared__ int32_t lds_ids[IDS];
-
-    const int g = blockIdx.x;
-    const int qt = a.n_qtiles - 1 - (int)blockIdx.y / a.ks;
-    const int ksp = (int)blockIdx.y % a.ks;          // key split of this workgroup
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 15, quad = lane >> 4;
-
-    // Sequences are taken longest context first (grid z is the rank), so the
-    // heaviest workgroups start first and the light ones fill the tail.
-    // Ranking is done for up to 64 sequences; beyond that, in order.
-    int s = blockIdx.z;
-    if (a.S <= 64) {
-        const int i = lane < a.S ? lane : 0;
-        const int wi = seq_len<BS>(a, i);
-        int rank = 0;
-        for (int j = 0; j < a.S; ++j) {
-            const int wj = __builtin_amdgcn_readlane(wi, j);
-            rank += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
-        }
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.S && rank == (int)blockIdx.z);
-        s = hit ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit)) : blockIdx.z;
-    }
-
-    const int q0 = a.syn_rows > 0 ? s * a.syn_rows : a.qsl[s];
-    const int C = a.syn_rows > 0 ? a.syn_rows : a.qsl[s + 1] - q0;
-    int L = seq_len<BS>(a, s);
-    const int cap = a.stride * BS;
-    if (a.syn_rows == 0 && (L < 0 || L > cap || L < C))
-        PKV_DBG_NOTE(kDbgLength);
-    L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int p0 = L - C;                            // keys before the chunk
-    const int tok0 = qt * TQ;
-    if (tok0 >= C)
-        return;
-    const int tok_end = min(C, tok0 + TQ);
-    const int kend = a.causal ? min(L, p0 + tok_end) : L;   // keys any row of this tile attends
-    const int NT = kend > 0 ? (kend + KT - 1) / KT : 0;
-    // Key split ksp takes tiles [t0, t1) of the NT; an empty split still
-    // writes its (zero, -inf) state.
-    const int t0 = (int)((int64_t)NT * ksp / a.ks);
-    const int t1 = (int)((int64_t)NT * (ksp + 1) / a.ks);
-
-    // This lane's two query columns (one per 16-row MFMA tile).
-    int lim[NCT];
-    bool valid[NCT];
-    int64_t qrow[NCT], qin[NCT];
-    const int qbase = a.q_shared ? 0 : q0;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int r = w * WROWS + ct * 16 + n;
-        const int tok = tok0 + r / G;
-        valid[ct] = tok < tok_end;
-        lim[ct] = valid[ct] ? (a.causal ? p0 + tok : L - 1) : -1;
-        qrow[ct] = ((int64_t)(q0 + tok) * a.Hq + g * G + r % G) * D;
-        qin[ct] = ((int64_t)(qbase + tok) * a.Hq + g * G + r % G) * D;
-    }
-    // Smallest key limit over the wave's valid rows (wave-uniform): a tile
-    // entirely at or below it needs no mask.
-    const int wtok = tok0 + (w * WROWS) / G;
-    const int lim_w = wtok < tok_end ? (a.causal ? p0 + wtok : L - 1) : 0x7FFFFFFF;
-
-    // Scores enter the exponent as fma(s, c, -m) with c = |scale| log2(e):
-    // for a negative scale the q operand's sign bits are flipped (exact), so
-    // the running max of s * c is c times the max of the raw scores.
-    // (c is kept away from 0 so that masked -inf scores still give 0.)
-    const float c = fmaxf(a.scale_log2 < 0.0f ? -a.scale_log2 : a.scale_log2, 1e-30f);
-    const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
-    bf16x8 qf[NCT][NDS];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-            // Unconditional load (row 0 for a padding column, which the
-            // chunk always has), so all of the wave's q loads are in flight
-            // together; a load under the condition was waited for alone.
-            // (The mask is applied arithmetically: a select lets the
-            // compiler move the load back under the condition.)
-            const uint4 v = *reinterpret_cast<const uint4 *>(
-                a.q + (valid[ct] ? qin[ct] : 0) + ds * 32 + quad * 8);
-            const uint32_t mk = 0u - (uint32_t)valid[ct];
-            const uint4 x = make_uint4((v.x ^ qsign) & mk, (v.y ^ qsign) & mk,
-                                       (v.z ^ qsign) & mk, (v.w ^ qsign) & mk);
-            qf[ct][ds] = __builtin_bit_cast(bf16x8, x);
-        }
-
-    const int32_t *bt = a.tables + (int64_t)s * a.stride;
-    const int64_t hstride = (int64_t)BS * D;         // elements per (block, head) tile
-    const int64_t bstride = (int64_t)a.Hkv * hstride;
-    const uint16_t *kg = a.kc + g * hstride;
-    const uint16_t *vg = a.vc + g * hstride;
-    const int nblk = (kend + BS - 1) / BS;           // blocks the workgroup reads
-
-    // Block ids of the key range staged through LDS, IDS at a time.
-    // All loads first (at a clamped index; nblk >= 1 whenever ids are
-    // staged), then the LDS stores, so the loads are in flight together.
-    auto stage_ids = [&](int chunk) {
-        constexpr int PER = IDS / kThreads;
-        int idv[PER];
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int jb = chunk * IDS + tid + k * kThreads;
-            idv[k] = bt[jb < nblk ? jb : nblk - 1];
-        }
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int jb = chunk * IDS + tid + k * kThreads;
-            if (jb < nblk && (unsigned)idv[k] >= (unsigned)a.num_blocks)
-                PKV_DBG_NOTE(kDbgBlockId);
-            lds_ids[tid + k * kThreads] = jb < nblk ? idv[k] : -1;
-        }
-    };
-
-    uint4 kst[Sh::KLD], vst[VK];
-    // Global loads of key tile kt into registers.  K: wave w reads part wp
-    // of block w / WPB of the tile (WPB = waves per block), one 1 KiB run of
-    // the block's (block, head) tile per load; K keeps each token's dims in
-    // 16-byte chunks (chunk c of token t at (c * BS + t) * 16 bytes).  V
-    // keeps 4 consecutive tokens of one dim together (element (t, d) at
-    // ((t / 4) * D + d) * 4 + t % 4, a 4-key group being one 8 D-byte run),
-    // and is read in pairs of groups: pair pr = 4 s2 + qd holds the groups of
-    // keys 32 s2 + 16 h + 4 qd .. + 3 for h = 0, 1, the two halves of one PV
-    // operand.  Wave w reads pairs 2 w and 2 w + 1 (so s2 = w / 2), each lane
-    // the same 16-byte unit (2 dims x 4 keys) of both groups of a pair, so
-    // that it can store both halves of a dim side by side.  Each load goes
-    // through a buffer resource on the wave's block held in scalar registers;
-    // a block id outside the pool, or a block past the context, gets an
-    // empty resource and reads zeros without touching memory.
-    constexpr int WPB = NW * BS / KT;                // waves per block of the tile
-    const int wblk = BS * (w / WPB);                 // the wave's first key in the tile
-    const int wp = w % WPB;
-    static_assert(VK * 64 == 2 * D, "two V group pairs per wave");
-    const int vs2 = w / 2;
-    int vquad[VK / 2], vu[VK / 2];
-#pragma unroll
-    for (int j = 0; j < VK / 2; ++j) {
-        const int cid = (w * (VK / 2) + j) * 64 + lane;
-        vquad[j] = (cid / (D / 2)) % 4;
-        vu[j] = cid % (D / 2);
-    }
-    auto tile_rsrc = [&](const uint16_t *base, int j) {
-        const int jj = __builtin_amdgcn_readfirstlane(j);
-        const int id = jj < L ? lds_ids[(jj / BS) % IDS] : -1;
-        const int ids = __builtin_amdgcn_readfirstlane(id);
-        const bool ok = (unsigned)ids < (unsigned)a.num_blocks;
-        return __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(base + (ok ? (int64_t)ids * bstride : 0)), 0,
-            ok ? (int)(hstride * 2) : 0, kRsrcWord3);
-    };
-    auto load_tile = [&](int kt) {
-        const auto rk = tile_rsrc(kg, kt * KT + wblk);
-#pragma unroll
-        for (int i = 0; i < Sh::KLD; ++i)
-            kst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rk, ((wp * Sh::KLD + i) * 64 + lane) * 16, 0, 0));
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const auto rv = tile_rsrc(vg, kt * KT + 32 * vs2 + (BS == 16 ? 16 * h : 0));
-#pragma unroll
-            for (int j = 0; j < VK / 2; ++j)
-                vst[2 * j + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rv, (BS == 16 ? vquad[j] : 4 * h + vquad[j]) * 8 * D + vu[j] * 16, 0, 0));
-        }
-        // Unused slots past the context end must not reach the PV product as
-        // NaN (0 * NaN = NaN): zero them (only the tile holding the end).
-        if (kt * KT + KT > L) {
-#pragma unroll
-            for (int j = 0; j < VK / 2; ++j)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int nv = L - (kt * KT + 32 * vs2 + 16 * h + 4 * vquad[j]);
-                    const uint32_t m01 = (nv > 0 ? 0x0000FFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
-                    const uint32_t m23 = (nv > 2 ? 0x0000FFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
-                    uint4 &x = vst[2 * j + h];
-                    x.x &= m01;
-                    x.y &= m23;
-                    x.z &= m01;
-                    x.w &= m23;
-                }
-        }
-    };
-    // Registers -> LDS buffer: K rows as they are (16-byte unit q of the
-    // wave's K part is chunk q / BS of token q % BS); V as [pair][D][8]: the
-    // 4 keys of dim d from the pair's first group, then its 4 keys from the
-    // second, so one 16-byte LDS read is one PV operand.
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < Sh::KLD; ++i) {
-            const int q = (wp * Sh::KLD + i) * 64 + lane;
-            const int kk = wblk + q % BS, cc = q / BS;
-            *reinterpret_cast<uint4 *>(&lds_k[buf][kk * KSTR + cc * 8]) = kst[i];
-        }
-#pragma unroll
-        for (int j = 0; j < VK / 2; ++j) {
-            uint16_t *v0 = &lds_v[buf][(4 * vs2 + vquad[j]) * VPS + 2 * vu[j] * 8];
-            const uint4 a = vst[2 * j], b = vst[2 * j + 1];
-            *reinterpret_cast<uint4 *>(v0) = make_uint4(a.x, a.y, b.x, b.y);
-            *reinterpret_cast<uint4 *>(v0 + 8) = make_uint4(a.z, a.w, b.z, b.w);
-        }
-    };
-
-    f32x4 o[NDT][NCT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-            o[dt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m[NCT], lsum[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        m[ct] = -INFINITY;
-        lsum[ct] = 0.0f;
-    }
-
-    if (t1 > t0) {
-        stage_ids(t0 / CT);
-        __syncthreads();
-        load_tile(t0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int kt = t0; kt < t1; ++kt) {
-        const int buf = (kt - t0) & 1;
-        if (kt + 1 < t1) {
-            if ((kt + 1) % CT == 0) {                // next tile starts a new id chunk
-                stage_ids((kt + 1) / CT);
-                __syncthreads();
-            }
-            load_tile(kt + 1);
-        }
-
-        // S^T tile: 64 keys x 32 query columns.
-        f32x4 sacc[4][NCT];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                sacc[ks][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                    &lds_k[buf][(ks * 16 + n) * KSTR + ds * 32 + quad * 8]);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    sacc[ks][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ct][ds],
-                                                                           sacc[ks][ct], 0, 0, 0);
-            }
-
-        // Online softmax per query column.  Lane holds keys
-        // kt*64 + ks*16 + 4*quad + i of column n.  Only tiles that cross the
-        // causal diagonal or the context end are masked (wave-uniform test,
-        // taken as a real branch).
-        const bool full = kt * KT + KT - 1 <= lim_w;
-        if (!full) [[unlikely]] {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (kt * KT + ks * 16 + quad * 4 + i > lim[ct])
-                            sacc[ks][ct][i] = -INFINITY;
-        }
-        bf16x8 phi[NCT][2], plo[NCT][2];
-        bool grew = false;
-        float alpha[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            // Max of the lane's 16 scores, two new values per 3-input step.
-            float mt = vmax(sacc[0][ct][0], vmax(sacc[0][ct][1], sacc[0][ct][2]));
-#pragma unroll
-            for (int k = 3; k < 15; k += 2)
-                mt = vmax(mt, vmax(sacc[k / 4][ct][k % 4], sacc[(k + 1) / 4][ct][(k + 1) % 4]));
-            mt = vmax(mt, sacc[3][ct][3]);
-            mt = xmax<16>(mt);
-            mt = xmax<32>(mt) * c;
-            const bool up = mt > m[ct] + kLazyMax;
-            const float mn = up ? mt : m[ct];
-            alpha[ct] = up ? __builtin_amdgcn_exp2f(m[ct] - mn) : 1.0f;
-            grew |= up;
-            m[ct] = mn;
-            // exp2(s c - m); a fully masked column so far (m = -inf) gets 0.
-            const float negm = mn == -INFINITY ? 0.0f : -mn;
-            float sum = 0.0f;
-            float pv[4][4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[ks][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ks][ct][i], c, negm));
-                    sum += pv[ks][i];
-                }
-            lsum[ct] = __builtin_fmaf(lsum[ct], alpha[ct], sum);
-            // P^T operands for the two 32-key k-steps: keys {32s + 4q + i}
-            // then {32s + 16 + 4q + i}.  hi = p truncated to bf16 (its top
-            // 16 bits, exact as an fp32 value), lo = bf16(p - hi): together
-            // they carry ~16 significant bits of p.
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const uint32_t u0 = __builtin_bit_cast(uint32_t, pv[2 * s2 + half][i]);
-                        const uint32_t u1 = __builtin_bit_cast(uint32_t, pv[2 * s2 + half][i + 1]);
-                        const float r0 = pv[2 * s2 + half][i] -
-                                         __builtin_bit_cast(float, u0 & 0xFFFF0000u);
-                        const float r1 = pv[2 * s2 + half][i + 1] -
-                                         __builtin_bit_cast(float, u1 & 0xFFFF0000u);
-                        hw[half * 2 + i / 2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                        lw[half * 2 + i / 2] = __builtin_bit_cast(
-                            uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2_t));
-                    }
-                phi[ct][s2] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-                plo[ct][s2] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-            }
-        }
-        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    o[dt][ct] *= alpha[ct];
-        }
-
-        // O^T += V^T P^T (hi and lo parts).  Each accumulator takes its hi
-        // product, then its lo product; the lo products of dims tile dt - 1
-        // are issued after the hi products of tile dt, so no MFMA waits for
-        // the one just before it to finish accumulating.
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            // A operand of dims dt*16 + n: k slots 8 quad + 4 half + i hold key
-            // 32 s2 + 16 half + 4 quad + i (the order of P^T's B operand): dim
-            // d of V group pair 4 s2 + quad.
-            auto vload = [&](int dt) {
-                return *reinterpret_cast<const bf16x8 *>(
-                    &lds_v[buf][(4 * s2 + quad) * VPS + (dt * 16 + n) * 8]);
-            };
-            bf16x8 vprev = vload(0);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                o[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vprev, phi[ct][s2], o[0][ct],
-                                                                   0, 0, 0);
-#pragma unroll
-            for (int dt = 1; dt < NDT; ++dt) {
-                const bf16x8 va = vload(dt);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    o[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[ct][s2],
-                                                                        o[dt][ct], 0, 0, 0);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    o[dt - 1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        vprev, plo[ct][s2], o[dt - 1][ct], 0, 0, 0);
-                vprev = va;
-            }
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                o[NDT - 1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    vprev, plo[ct][s2], o[NDT - 1][ct], 0, 0, 0);
-        }
-
-        if (kt + 1 < t1)
-            store_tile(buf ^ 1);
-        __syncthreads();
-    }
-
-    // Normalise and write: lane holds O^T[dt*16 + 4*quad + i][column n].
-    // With key splits the output is split ksp's fp32 state.
-    float *const lse_out = a.lse ? a.lse + ksp * a.split_rows : nullptr;
-    void *const out = a.ks > 1 ? static_cast<void *>(static_cast<float *>(a.out) +
-                                                     ksp * a.split_rows * D)
-                               : a.out;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        float l = lsum[ct];
-        l = xsum<16>(l);
-        l = xsum<32>(l);
-        // (A split's state has S * max_query_len rows: rows past that exist
-        // only if a chunk exceeds max_query_len, and are not written.)
-        if (!valid[ct] || (a.ks > 1 && qrow[ct] / D >= a.split_rows))
-            continue;
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        if (lse_out && quad == 0)
-            lse_out[qrow[ct] / D] = l > 0.0f ? m[ct] + __log2f(l) : -INFINITY;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const int64_t idx = qrow[ct] + dt * 16 + quad * 4;
-            const f32x4 r = o[dt][ct] * inv;
-            if (a.out_dtype == PKV_F32) {
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + idx) = r;
-            } else {
-                uint2 pk;
-                pk.x = (uint32_t)bf16_rne(r[0]) | ((uint32_t)bf16_rne(r[1]) << 16);
-                pk.y = (uint32_t)bf16_rne(r[2]) | ((uint32_t)bf16_rne(r[3]) << 16);
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + idx) = pk;
-            }
-        }
-    }
-}
-
-
-// Software-pipelined variant (block tables of up to kIdChunk entries):
-// same workgroup shape, layouts, softmax and hi/lo P split as k_prefill,
-// but the work of consecutive key tiles overlaps inside each wave.  The
-// body for tile kt runs the PV product of tile kt - 1 beside the softmax of
-// tile kt, and the S product of tile kt + 1 beside the P split of tile kt,
-// so that the matrix cores and the vector units have independent work at
-// every point; one LDS-only barrier per tile.  K is staged two tiles ahead
-// and V one (K tile t and V tile t in LDS buffer t & 1), through registers
-// loaded one tile earlier.  The first tile's PV is that of an all-zero P
-// over a zeroed V buffer.
+// The loop: the body for tile kt runs the PV product of tile kt - 1 beside
+// the softmax of tile kt, and the S product of tile kt + 1 beside the P
+// split of tile kt, so that the matrix cores and the vector units have
+// independent work at every point.  K is staged two tiles ahead and V one
+// (K tile t and V tile t in LDS buffer t & 1), through registers loaded one
+// tile earlier.  The first tile's PV is that of an all-zero P over a
+// zeroed V buffer.
 // Workgroup barrier ordering LDS only (global loads in flight stay in flight).
 __device__ __forceinline__ void lds_barrier_pf()
 {
@@ -590,14 +170,14 @@ __device__ __forceinline__ void lds_barrier_pf()
 }
 
 template <int D, int BS, int G>
-__global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs a)
+__global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
 {
     using Sh = PShape<D>;
     constexpr int TQ = ROWS / G;                     // chunk tokens per workgroup
     constexpr int NDS = Sh::NDS, NDT = Sh::NDT, CPR = Sh::CPR, VK = Sh::VK;
     constexpr int KSTR = Sh::KSTR, VPS = Sh::VPS;
-    constexpr int IDS = kIdChunk;                    // block ids staged per chunk
-    constexpr int CT = IDS * BS / KT;                // key tiles per id chunk
+    constexpr int IDS = kIdChunk;                    // ring of block ids in LDS
+    constexpr int IPT = KT / BS;                     // block ids per key tile
 
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][Sh::KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][Sh::VBUF];
@@ -695,24 +275,36 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
     const uint16_t *vg = a.vc + g * hstride;
     const int nblk = (kend + BS - 1) / BS;           // blocks the workgroup reads
 
-    // Block ids of the key range staged through LDS, IDS at a time.
-    // All loads first (at a clamped index; nblk >= 1 whenever ids are
-    // staged), then the LDS stores, so the loads are in flight together.
-    auto stage_ids = [&](int chunk) {
+    // Block ids live in a ring of IDS slots (block j at slot j % IDS),
+    // two halves of HALF key tiles: the key range's first 2 HALF tiles are
+    // staged at the start, and when the loop enters a new half, the half
+    // it has left is restaged with the ids HALF tiles further on, used only
+    // after many per-tile barriers.  Tables of any length stream through.
+    constexpr int HALF = IDS / IPT / 2;
+    auto id_at = [&](int jb) {
+        const int v = bt[jb < nblk ? jb : (nblk > 0 ? nblk - 1 : 0)];
+        if (jb < nblk && (unsigned)v >= (unsigned)a.num_blocks)
+            PKV_DBG_NOTE(kDbgBlockId);
+        return jb < nblk ? v : -1;
+    };
+    auto stage_ids = [&](int t, int count) {       // ids of count tiles from tile t
         constexpr int PER = IDS / kThreads;
         int idv[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int jb = chunk * IDS + tid + k * kThreads;
-            idv[k] = bt[jb < nblk ? jb : nblk - 1];
+            const int i = tid + k * kThreads;
+            idv[k] = i < count * IPT ? id_at(t * IPT + i) : -1;
         }
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int jb = chunk * IDS + tid + k * kThreads;
-            if (jb < nblk && (unsigned)idv[k] >= (unsigned)a.num_blocks)
-                PKV_DBG_NOTE(kDbgBlockId);
-            lds_ids[tid + k * kThreads] = jb < nblk ? idv[k] : -1;
+            const int i = tid + k * kThreads;
+            if (i < count * IPT)
+                lds_ids[(t * IPT + i) & (IDS - 1)] = idv[k];
         }
+    };
+    auto restage = [&](int kt) {
+        if (kt > t0 && ((kt - t0) & (HALF - 1)) == 0)
+            stage_ids(kt + HALF, HALF);
     };
 
     uint4 kst[Sh::KLD], vst[VK];
@@ -963,6 +555,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
     // buffer resources, into buffers no later tile reads.
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     auto tile_full = [&](int kt) {
+        restage(kt);
         if (__builtin_amdgcn_ballot_w64(grew) != 0) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
@@ -1106,6 +699,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
     // same steps in plain order, with the mask, the V zeroing past the
     // context end and range checks on the staging.
     auto tile_masked = [&](int kt) {
+        restage(kt);
         if (__builtin_amdgcn_ballot_w64(grew) != 0) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
@@ -1130,7 +724,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
     };
 
     if (t1 > t0) {
-        stage_ids(t0 / CT);
+        stage_ids(t0, 2 * HALF);
         __syncthreads();
         load_k(t0);
         store_k(t0);
@@ -1209,32 +803,13 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill_sp(PArgs
 using KernelFn = void (*)(PArgs);
 
 template <int D, int BS>
-KernelFn pick_g(int G)
+KernelFn pick_sp_g(int G)
 {
     switch (G) {
     case 1: return k_prefill<D, BS, 1>;
     case 2: return k_prefill<D, BS, 2>;
     case 4: return k_prefill<D, BS, 4>;
     case 8: return k_prefill<D, BS, 8>;
-    default: return nullptr;
-    }
-}
-
-KernelFn pick(int D, int BS, int G)
-{
-    if (D == 64)
-        return BS == 16 ? pick_g<64, 16>(G) : pick_g<64, 32>(G);
-    return BS == 16 ? pick_g<128, 16>(G) : pick_g<128, 32>(G);
-}
-
-template <int D, int BS>
-KernelFn pick_sp_g(int G)
-{
-    switch (G) {
-    case 1: return k_prefill_sp<D, BS, 1>;
-    case 2: return k_prefill_sp<D, BS, 2>;
-    case 4: return k_prefill_sp<D, BS, 4>;
-    case 8: return k_prefill_sp<D, BS, 8>;
     default: return nullptr;
     }
 }
@@ -1255,7 +830,7 @@ int launch_prefill(const PrefillLaunch &p)
     if (p.num_seqs == 0 || p.max_query_len == 0)
         return PKV_OK;
     const int G = p.num_q_heads / p.num_kv_heads;
-    KernelFn fn = pick(p.head_dim, p.block_size, G);
+    KernelFn fn = pick_sp(p.head_dim, p.block_size, G);
     if (!fn)
         return fail(PKV_EUNSUPPORTED, "pkv_prefill_chunk: no kernel for head_dim %d, block %d, "
                     "group %d", p.head_dim, p.block_size, G);
@@ -1292,10 +867,6 @@ int launch_prefill(const PrefillLaunch &p)
     a.syn_nbk = p.syn_nbk;
     a.syn_nb = p.syn_nb;
     hipStream_t st = reinterpret_cast<hipStream_t>(p.stream);
-    // The software-pipelined kernel keeps every block id of a sequence in
-    // one LDS list; longer tables take the kernel that restages the ids.
-    if (p.table_stride <= kIdChunk)
-        fn = pick_sp(p.head_dim, p.block_size, G);
     hipLaunchKernelGGL(fn, dim3(p.num_kv_heads, (unsigned)(nqt * ks), p.num_seqs), dim3(kThreads),
                        0, st, a);
     hipError_t e = hipGetLastError();
