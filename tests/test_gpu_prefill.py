@@ -89,12 +89,14 @@ def test_empty_chunk_and_max_query_len_above_every_chunk(split):
 
 
 @pytest.mark.parametrize("split", [False, True])
-def test_block_table_longer_than_one_id_list(split):
-    # More than 1024 blocks in a sequence's table: the kernel that restages
-    # block ids in chunks (the pipelined one keeps them in one LDS list).
-    b = synth.custom_prefill(319, prior=[17000, 30], chunk=[40, 9], Hq=16, Hkv=2, D=128,
-                             block_size=16)
-    say(f"[prefill] long table ({int(b.lens.max()) // 16 + 1} blocks), split={split}")
+@pytest.mark.parametrize("bs,prior", [(16, 17000), (32, 33000)])
+def test_block_table_longer_than_the_id_ring(split, bs, prior):
+    # More than 1024 blocks in a sequence's table: the kernel's LDS ring of
+    # block ids is restaged as the loop moves on (more than 2 x 128 key tiles
+    # at block 16, 2 x 256 at block 32).
+    b = synth.custom_prefill(319, prior=[prior, 30], chunk=[40, 9], Hq=16, Hkv=2, D=128,
+                             block_size=bs)
+    say(f"[prefill] long table ({int(b.lens.max()) // bs + 1} blocks), bs={bs}, split={split}")
     cache, q, qs, tab, lens, mx = prefill_state(b)
     assert tab.shape[1] > 1024
     out = run_prefill(cache, q, qs, tab, lens, mx, b.shape.scale, 40, split=split)
