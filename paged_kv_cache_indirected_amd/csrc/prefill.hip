@@ -154,6 +154,14 @@ __device__ __forceinline__ float xsum(float v)
     return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
 }
 
+// Workgroup barrier ordering LDS only (global loads in flight stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The loop: the body for tile kt runs the PV product of tile kt - 1 beside
 // the softmax of tile kt, and the S product of tile kt + 1 beside the P
 // split of tile kt, so that the matrix cores and the vector units have
@@ -161,14 +169,6 @@ __device__ __forceinline__ float xsum(float v)
 // (K tile t and V tile t in LDS buffer t & 1), through registers loaded one
 // tile earlier.  The first tile's PV is that of an all-zero P over a
 // zeroed V buffer.
-// Workgroup barrier ordering LDS only (global loads in flight stay in flight).
-__device__ __forceinline__ void lds_barrier_pf()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
 {
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 sacc[ks][ct] = snew[ks][ct];
-        lds_barrier_pf();
+        lds_barrier();
     };
 
     // A tile some row masks (the causal diagonal, or the context end): the
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(kThreads, NCT == 2 ? 2 : 1) void k_prefill(PArgs a)
             load_k(kt + 3);
         if (kt + 1 < t1)
             load_v(kt + 1);
-        lds_barrier_pf();
+        lds_barrier();
     };
 
     if (t1 > t0) {
